@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark: one full Muon optimizer step on Qwen3-4B-shaped matrices.
+
+A step = momentum (+ Nesterov) -> batched Newton-Schulz (5 quintic
+iterations, bf16 MFMA) -> apply (fp32 master + bf16 copy) over all 252 Muon
+matrices of a 36-layer Qwen3-4B (3.63B parameters), in 512 MiB micro-buckets.
+Inputs are synthetic and already resident in HBM (bf16 gradients ~ N(0, 1e-3),
+fp32 momentum pre-filled by two momentum steps, fp32 masters ~ N(0, 0.02)).
+
+Prints ONE JSON line.  `value` is Newton-Schulz algorithmic TFLOP per step
+divided by the whole step's wall time; ms_per_step is the full step.  Per-
+kernel durations come from HIP events the library records on the launch
+stream around every kernel during the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Newton–Schulz TFLOP/s (% bf16 MFMA peak); full Muon step ms, Qwen3-4B shapes"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def ns_flops(m: int, n: int, steps: int = 5):
+    """Algorithmic flops of one unit (m <= n): symmetric Gram m(m+1)n, symmetric
+    square m^2(m+1), update 2 m^2 n, per iteration."""
+    gram = m * (m + 1) * n
+    symsq = m * m * (m + 1)
+    upd = 2 * m * m * n
+    return steps * gram, steps * symsq, steps * upd
+
+
+def workload_by_name(name):
+    from newton_schulz_amd import synth
+    if name == "qwen3_4b":
+        return synth.qwen3_4b()
+    if name == "qwen3_4b_layer":
+        return synth.qwen3_4b_layer()
+    if name == "qwen3_4b_heads":
+        return synth.qwen3_4b_heads()
+    if name.startswith("qwen3_30b_experts"):
+        layers = int(name.split(":")[1]) if ":" in name else 4
+        return synth.qwen3_30b_experts(layers=layers)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def unit_list(w):
+    units = []
+    for m in w.mats:
+        if m.zero_grad:
+            continue
+        ur = m.head_rows or m.rows
+        for _ in range(m.rows // ur):
+            units.append((min(ur, m.cols), max(ur, m.cols)))
+    return units
+
+
+def traffic_record(kernel_src: str):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    counter summary, or None when missing or taken on a different source."""
+    path = os.path.join(ROOT, "profiles", "update_kernel_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
+    if rec.get("source_sha256_16") != h:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(seconds_budget: float = 20.0):
+    """The oracle (numpy fp64 Newton-Schulz, binary32 momentum/apply) on one
+    Qwen3-4B layer, timed on this host's cores."""
+    import numpy as np
+    import oracle
+    from newton_schulz_amd import synth
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    ctxm = threadpool_limits(limits=cores, user_api="blas") if threadpool_limits else None
+    w = synth.qwen3_4b_layer()
+    rng = np.random.default_rng(0)
+    mats = [(m.rows, m.cols) for m in w.mats]
+    t_ns = t_el = 0.0
+    flops = 0
+    done = 0
+    try:
+        for (r, c) in mats:
+            g = oracle.bf16_round((rng.standard_normal((r, c)) * 1e-3).astype(np.float32))
+            M = np.zeros((r, c), np.float32)
+            W = (rng.standard_normal((r, c)) * 0.02).astype(np.float32)
+            t0 = time.perf_counter()
+            M, U = oracle.momentum_ref(g, M, 0.95, True)
+            t1 = time.perf_counter()
+            O = oracle.ns_ref(oracle.bf16_round(U))
+            t2 = time.perf_counter()
+            oracle.apply_ref(W, oracle.bf16_round(O.astype(np.float32)), 0.02, bf16_copy=True)
+            t3 = time.perf_counter()
+            t_el += (t1 - t0) + (t3 - t2)
+            t_ns += t2 - t1
+            flops += sum(ns_flops(min(r, c), max(r, c)))
+            done += 1
+            if t_ns + t_el > seconds_budget:
+                break
+        blas = None
+        if threadpool_limits:
+            info = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+            blas = info[0].get("internal_api") if info else None
+            cores_used = info[0].get("num_threads", cores) if info else cores
+        else:
+            cores_used = cores
+    finally:
+        if ctxm is not None:
+            ctxm.__exit__(None, None, None)
+    tot = t_ns + t_el
+    return {
+        "value": round(flops / tot / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores_used),
+        "kind": "oracle",
+        "sample": f"{done} of the 7 matrices of one Qwen3-4B layer (q, k, v, o, gate, up, down): "
+                  f"momentum + fp64 Newton-Schulz + apply; {tot:.1f} s on the host "
+                  f"(NS {t_ns:.1f} s); BLAS {blas}",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_4b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-timing", action="store_true", help="skip per-kernel event timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from newton_schulz_amd import MuonStep, synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    w = workload_by_name(args.workload)
+    shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
+    keep_bf16 = args.workload != "qwen3_30b_experts"
+    ms = MuonStep(shapes, dev, lr=w.lr, beta=w.beta, nesterov=w.nesterov, compute=w.compute,
+                  grad_dtype=w.grad_dtype, cap_bytes=w.cap_bytes, cap_kind=w.cap_kind,
+                  ns_steps=w.ns_steps, keep_bf16_weights=keep_bf16)
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    for i, W0 in enumerate(synth.draw_weights(w, g, dev)):
+        ms.view(ms.master, i).copy_(W0)
+    grads = [ms.view(ms.grad, i) for i in range(len(w.mats))]
+    for _ in range(w.warmup_momentum_steps):
+        synth.draw_grads(w, g, dev, out=grads)
+        ms.momentum_only()
+    synth.draw_grads(w, g, dev, out=grads)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        ms.step()
+    torch.cuda.synchronize()
+
+    timing = not args.no_timing
+    if timing:
+        ms.ctx.timing_enable(True, capacity=max(4096, args.steps * 2048))
+        ms.ctx.timing_reset()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        ms.step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    kt = ms.ctx.timing_read() if timing else {}
+
+    units = unit_list(w)
+    fl = [ns_flops(m, n, w.ns_steps) for (m, n) in units]
+    f_gram = sum(f[0] for f in fl)
+    f_symsq = sum(f[1] for f in fl)
+    f_upd = sum(f[2] for f in fl)
+    f_ns = f_gram + f_symsq + f_upd
+    dense = sum(w.ns_steps * (2 * m * m * n + 2 * m ** 3 + 2 * m * m * n) for (m, n) in units)
+    value = f_ns / (ms_per_step * 1e-3) / 1e12
+    numel = sum(m.numel for m in w.mats)
+    gdt_b = 2 if w.grad_dtype == torch.bfloat16 else 4
+    cdt_b = 2 if w.compute == "bf16" else 4
+    mom_bytes = numel * (gdt_b + 4 + 4 + cdt_b)
+    app_bytes = numel * (4 + 4 + cdt_b + (2 if keep_bf16 else 0))
+
+    breakdown = {}
+    roofline = None
+    if timing:
+        per_step = {k: (v[0] / args.steps, v[1] / args.steps) for k, v in kt.items()}
+        for k, (t, n) in per_step.items():
+            breakdown[k] = {"ms_per_step": round(t, 4), "launches_per_step": n}
+        def tf(f, k):
+            t = per_step[k][0]
+            return round(f / (t * 1e-3) / 1e12, 2) if t > 0 else None
+        breakdown["gram"]["tflops"] = tf(f_gram, "gram")
+        breakdown["symsq"]["tflops"] = tf(f_symsq, "symsq")
+        breakdown["update"]["tflops"] = tf(f_upd, "update")
+        ns_ms = sum(per_step[k][0] for k in ("norm", "gram", "symsq", "update"))
+        breakdown["newton_schulz"] = {"ms_per_step": round(ns_ms, 4),
+                                      "tflops": round(f_ns / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None}
+        for k, b in (("momentum", mom_bytes), ("apply", app_bytes)):
+            t = per_step[k][0]
+            breakdown[k]["gbs"] = round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
+            breakdown[k]["frac_hbm"] = round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if t > 0 else None
+        t_upd, n_upd = per_step["update"]
+        if n_upd > 0 and t_upd > 0:
+            achieved = f_upd / (t_upd * 1e-3) / 1e12
+            traffic = traffic_record(os.path.join(ROOT, "newton_schulz_amd", "csrc", "ns_gemm_mfma.hip"))
+            roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                        "traffic": traffic, "kernel": "ns_gemm_mfma_kernel (update X' = a X + B X)",
+                        "avg_launch_ms": round(t_upd / n_upd, 4),
+                        "flop_per_launch_avg": int(f_upd / n_upd)}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1e-3) bf16 gradients, fp32 state; no checkpoint)",
+        "config": {"workload": w.name, "matrices": len(w.mats), "muon_params": numel,
+                   "ns_units": len(units), "ns_steps": w.ns_steps,
+                   "micro_bucket_cap_bytes": w.cap_bytes, "cap_kind": w.cap_kind,
+                   "micro_buckets": len(ms.plan.buckets), "workspace_bytes": ms.plan.max_workspace,
+                   "parallelism": "single GPU"},
+        "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "ns_tflop_per_step_algorithmic": round(f_ns / 1e12, 4),
+        "ns_tflop_per_step_dense_equiv": round(dense / 1e12, 4),
+        "matrices_per_s": round(len(units) / (ms_per_step * 1e-3), 1),
+        "wall_s_timed": round(wall, 3),
+        "breakdown": breakdown,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

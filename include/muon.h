@@ -1,0 +1,233 @@
+/*
+ * libmuon -- the Muon optimizer step's hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The step, per whole 2D weight matrix (blog "Muon Optimizer + FSDP",
+ * section "Background: the conflict between FSDP and Muon"):
+ *
+ *     M_t = momentum_update(grad)      -> muon_momentum_update
+ *     U_t = NewtonSchulz(M_t)          -> muon_newton_schulz_batched
+ *     W_t = W_t - lr * U_t             -> muon_apply
+ *
+ * Conventions shared by every entry point
+ *   - Tensor arguments are DEVICE pointers to memory the caller owns and
+ *     keeps alive until the work enqueued on `stream` has finished.  Matrices
+ *     are dense row-major (rows x cols, leading dimension = cols).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *     stream of the context's device).  Every call only enqueues work; none
+ *     synchronises the device, none allocates device memory.
+ *   - Arguments are validated before anything is enqueued: on any status
+ *     other than MUON_OK nothing was launched.  Faults inside kernels surface
+ *     at the caller's next synchronisation, as for any HIP kernel.
+ *   - No C++ exception crosses this boundary.
+ *   - A context is not thread-safe; use one context per stream (calls made
+ *     on different streams with one context must be ordered by the caller).
+ */
+#ifndef LIBMUON_MUON_H
+#define LIBMUON_MUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MUON_OK = 0,
+  MUON_EINVAL = 1,      /* null pointer, bad count/size, aliasing, bad parameter */
+  MUON_ESHAPE = 2,      /* rows/cols <= 0, rows % head_rows != 0, ...           */
+  MUON_EDTYPE = 3,      /* dtype or dtype combination not supported             */
+  MUON_EWORKSPACE = 4,  /* the call needs more workspace than the context holds */
+  MUON_EHIP = 5,        /* a HIP runtime call failed (see muon_last_error)      */
+  MUON_ENOMEM = 6       /* host-side allocation failed                          */
+} muon_status_t;
+
+typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
+
+/* Newton-Schulz parameters.  The quintic iteration is the one the DeepSpeed
+ * RFC "Enable Correct and High-Performance Muon Optimizer under ZeRO CPU
+ * Offload" calls the current default (section 5, Roadmap), run for 5~6
+ * iterations (section 2, Root Cause Analysis).  Per iteration, on the
+ * normalised matrix X (m x n, m <= n):
+ *     A = X X^T ;  B = b A + c A A ;  X <- a X + B X
+ * X_0 = Y / (||Y||_F + eps); a tall Y (rows > cols) is processed as Y^T and
+ * the result transposed back.  Defaults (muon_ns_params_default):
+ * steps 5, (a, b, c) = (3.4445, -4.7750, 2.0315), eps 1e-7, compute BF16. */
+typedef struct {
+  int32_t steps;     /* >= 0 */
+  float a, b, c;     /* quintic coefficients */
+  float eps;         /* added to the Frobenius norm, >= 0 */
+  int32_t compute;   /* muon_dtype_t: BF16 = bf16 MFMA with fp32 accumulate,
+                        F32 = fp32 verification mode */
+} muon_ns_params_t;
+
+/* Geometry of one weight matrix (RFC section 4A: keep the 2D shape and head
+ * dimensions with the parameter).  head_rows = 0: the whole matrix is one
+ * Newton-Schulz unit; head_rows = h > 0: rows/h contiguous row blocks of
+ * h x cols are orthogonalised independently (RFC section 4D, per-head Muon;
+ * blog section "Chunked communication": split fused tensors into their
+ * logical matrices, never row-split one matrix). */
+typedef struct {
+  int64_t rows, cols, head_rows;
+} muon_shape_t;
+
+typedef struct muon_ctx muon_ctx_t;
+typedef struct muon_plan muon_plan_t;
+
+/* ------------------------------------------------------------------------ */
+/* Context and workspace                                                     */
+/* ------------------------------------------------------------------------ */
+
+/* Create a context on HIP device `device` holding one preallocated device
+ * workspace slab of `workspace_bytes` (blog section "Memory control", item 2:
+ * preallocate the workspace once and only take views of it per micro-bucket).
+ * This is the only call that allocates device memory.  On success *out owns
+ * the slab until muon_destroy.  Errors: MUON_EINVAL (out NULL),
+ * MUON_EHIP (no such device / allocation failed), MUON_ENOMEM. */
+muon_status_t muon_create(int device, size_t workspace_bytes, muon_ctx_t** out);
+
+/* Free the context and its workspace.  Waits for the context's device to
+ * finish the work enqueued so far.  NULL is accepted. */
+muon_status_t muon_destroy(muon_ctx_t* ctx);
+
+/* Size of the context's workspace slab in bytes (0 for NULL). */
+size_t muon_ctx_workspace_bytes(const muon_ctx_t* ctx);
+
+/* Fill *p with the defaults listed above. */
+void muon_ns_params_default(muon_ns_params_t* p);
+
+/* Workspace one muon_newton_schulz_batched call needs for `count` matrices
+ * of `shape` in compute dtype `compute` (pure host function).  Per Newton-
+ * Schulz unit of m x n (m = min, n = max of its rows and cols, e = element
+ * bytes of the compute dtype): two X buffers (2 e m n) + A and B (2 e m^2) +
+ * 8 bytes of scalars, each region rounded up to 256 bytes.  Returns 0 for an
+ * invalid shape. */
+size_t muon_ns_workspace_bytes(muon_shape_t shape, int64_t count, int32_t compute);
+
+/* ------------------------------------------------------------------------ */
+/* Host scheduler: same-shape buckets split into micro-buckets under a cap   */
+/* ------------------------------------------------------------------------ */
+
+typedef enum {
+  MUON_CAP_FULL_BYTES = 0,  /* sum of full-matrix bytes (e * rows * cols) <= cap */
+  MUON_CAP_WORKSPACE = 1    /* sum of Newton-Schulz workspace bytes      <= cap */
+} muon_cap_kind_t;
+
+typedef struct {
+  int64_t m, n;               /* canonical shape of the bucket's units (m <= n) */
+  int64_t count;              /* matrices in this micro-bucket                 */
+  int64_t units;              /* Newton-Schulz units (heads expanded)          */
+  int64_t numel;              /* elements of its matrices                      */
+  size_t full_bytes;          /* e * numel                                      */
+  size_t workspace_bytes;     /* sum of muon_ns_workspace_bytes per shape group */
+  int32_t over_cap;           /* 1 if a single matrix alone exceeds the cap     */
+  int32_t shape_groups;       /* distinct (rows, cols, head_rows) runs inside   */
+} muon_bucket_info_t;
+
+/* Group `count` matrices into buckets by canonical unit shape (m, n) in order
+ * of first appearance (blog section "Memory control", item 6: merge same-shape
+ * matrices across layers into one bucket), order each bucket's members by
+ * exact shape (stable), and cut each bucket into micro-buckets of whole
+ * matrices whose cost stays within `cap_bytes` (blog sections "Chunked
+ * communication" and "Memory control", item 1: a separate Muon cap;
+ * estimate_muon_peak(bucket) <= cap).  A matrix larger than the cap gets a
+ * micro-bucket of its own, flagged over_cap.  Host only; *out is owned by
+ * the caller (muon_plan_destroy).  Errors: MUON_EINVAL, MUON_ESHAPE. */
+muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t count, size_t cap_bytes,
+                               int32_t cap_kind, int32_t compute, muon_plan_t** out);
+int64_t muon_plan_num_buckets(const muon_plan_t* plan);
+/* Info on micro-bucket `b`; when `indices` is non-NULL it receives info->count
+ * matrix indices (positions in the `shapes` array), in execution order. */
+muon_status_t muon_plan_bucket(const muon_plan_t* plan, int64_t b, muon_bucket_info_t* info,
+                               int64_t* indices);
+/* Largest workspace_bytes over the plan's micro-buckets: a context this large
+ * runs every micro-bucket. */
+size_t muon_plan_max_workspace(const muon_plan_t* plan);
+void muon_plan_destroy(muon_plan_t* plan);
+
+/* ------------------------------------------------------------------------ */
+/* The three steps                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Momentum with Nesterov look-ahead over `numel` contiguous elements
+ * (blog, section "Background": M_t = momentum_update(grad); RFC section 2:
+ * the first-order momentum the offload path must keep).  Per element, each
+ * operation one IEEE binary32 rounding, no fused multiply-add:
+ *     t  = (1 - beta) * g
+ *     M' = beta * M + t                      (written back to momentum)
+ *     U  = t + beta * M'   (nesterov != 0)   or   U = M'   (nesterov == 0)
+ * grad: `grad_dtype` (BF16 or F32); momentum: F32, updated in place;
+ * update_out: `update_dtype` (BF16 = U rounded to nearest-even, or F32).
+ * numel == 0 is a no-op.  update_out may not alias grad or momentum; all
+ * pointers must be element-aligned.  Errors: MUON_EINVAL (NULL pointer,
+ * numel < 0, aliasing, beta outside [0, 1]), MUON_EDTYPE, MUON_EHIP. */
+muon_status_t muon_momentum_update(muon_ctx_t* ctx, void* stream, const void* grad,
+                                   int32_t grad_dtype, float* momentum, void* update_out,
+                                   int32_t update_dtype, int64_t numel, float beta,
+                                   int32_t nesterov);
+
+/* Batched Newton-Schulz over one same-shape group (blog section "Chunked
+ * communication": every Muon unit stays a whole matrix; XTuner-style same-
+ * shape buckets).  mats: HOST array of `count` device pointers to rows x cols
+ * matrices of io_dtype; out: HOST array of `count` device pointers receiving
+ * the orthogonalised update in the same shape and dtype (out == NULL, or
+ * out[i] == mats[i], means in place).  With shape.head_rows = h > 0 every
+ * h x cols row block is orthogonalised on its own.  Supported (io_dtype,
+ * params->compute): (BF16, BF16) -- bf16 MFMA, fp32 accumulate, A, B and
+ * the X iterates rounded to bf16; (F32, F32) -- fp32 verification mode.
+ * The Frobenius norm is reduced deterministically (fixed order), so two
+ * calls on identical inputs give identical bits.  A unit whose norm is 0
+ * yields exactly 0.  nonfinite_flag (device int, may be NULL) gets 1 OR-ed
+ * in when some unit's norm is not finite; values are propagated, never
+ * skipped.  Uses the context workspace (muon_ns_workspace_bytes(shape,
+ * count, compute) bytes).  count == 0 is a no-op.  Errors: MUON_EINVAL,
+ * MUON_ESHAPE, MUON_EDTYPE, MUON_EWORKSPACE, MUON_EHIP. */
+muon_status_t muon_newton_schulz_batched(muon_ctx_t* ctx, void* stream, const void* const* mats,
+                                         int64_t count, muon_shape_t shape, int32_t io_dtype,
+                                         const muon_ns_params_t* params, void* const* out,
+                                         int* nonfinite_flag);
+
+/* Weight apply over `numel` contiguous elements (blog, section "Background":
+ * W_t = W_t - lr * U_t).  Each operation one binary32 rounding, no FMA:
+ *     eta = lr * scale;  W1 = W * (1 - lr * weight_decay) if weight_decay != 0
+ *     W'  = W1 - eta * u                        (written back to master)
+ *     weight_bf16 = W' rounded to nearest-even  (when weight_bf16 != NULL)
+ * update: `update_dtype` (BF16 or F32).  numel == 0 is a no-op.
+ * Errors: MUON_EINVAL (NULL master/update, numel < 0, aliasing),
+ * MUON_EDTYPE, MUON_EHIP. */
+muon_status_t muon_apply(muon_ctx_t* ctx, void* stream, float* master, const void* update,
+                         int32_t update_dtype, void* weight_bf16, int64_t numel, float lr,
+                         float scale, float weight_decay);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+
+const char* muon_status_string(muon_status_t s);
+/* Text of the last error recorded on ctx (empty string when none). */
+const char* muon_last_error(const muon_ctx_t* ctx);
+
+/* Per-kernel-class timing with HIP events recorded on the launch stream
+ * around each kernel (per-bucket timing, blog section "Metrics to record").
+ * enable != 0 preallocates an event pool; launches beyond its capacity are
+ * not timed.  muon_timing_read synchronises on the recorded events and
+ * returns the summed duration and number of timed launches of one class. */
+typedef enum {
+  MUON_K_MOMENTUM = 0,
+  MUON_K_NORM = 1,
+  MUON_K_GRAM = 2,
+  MUON_K_SYMSQ = 3,
+  MUON_K_UPDATE = 4,
+  MUON_K_APPLY = 5,
+  MUON_K_COUNT = 6
+} muon_kernel_class_t;
+
+muon_status_t muon_timing_enable(muon_ctx_t* ctx, int32_t enable, int32_t capacity);
+muon_status_t muon_timing_reset(muon_ctx_t* ctx);
+muon_status_t muon_timing_read(muon_ctx_t* ctx, int32_t kernel_class, double* total_ms,
+                               int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LIBMUON_MUON_H */

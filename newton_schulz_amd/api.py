@@ -1,0 +1,223 @@
+"""Python binding of libmuon: argument marshalling only.
+
+Every step of the optimizer runs in the HIP kernels behind include/muon.h;
+PyTorch supplies device memory and the current HIP stream.  When libmuon.so
+is missing the calls raise instead of falling back to any other code.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import MUON_BF16, MUON_CAP_FULL_BYTES, MUON_CAP_WORKSPACE, MUON_F32, NsParams, Shape
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, msg: str = ""):
+        lib = _lib.load()
+        text = lib.muon_status_string(status).decode()
+        super().__init__(f"libmuon status {status} ({text}){': ' + msg if msg else ''}")
+        self.status = status
+
+
+_DT = {torch.float32: MUON_F32, torch.bfloat16: MUON_BF16}
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}; libmuon takes float32 or bfloat16")
+    return _DT[t.dtype]
+
+
+def _stream(device: torch.device, stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, device: torch.device):
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be a tensor on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def ns_params(steps: int = 5, a: float = 3.4445, b: float = -4.7750, c: float = 2.0315,
+              eps: float = 1e-7, compute: str = "bf16") -> NsParams:
+    return NsParams(steps, a, b, c, eps, MUON_BF16 if compute == "bf16" else MUON_F32)
+
+
+def ns_workspace_bytes(rows: int, cols: int, count: int, head_rows: int = 0,
+                       compute: str = "bf16") -> int:
+    return int(_lib.load().muon_ns_workspace_bytes(
+        Shape(rows, cols, head_rows), count, MUON_BF16 if compute == "bf16" else MUON_F32))
+
+
+class Context:
+    """A libmuon context: one device and one preallocated workspace slab."""
+
+    def __init__(self, device=None, workspace_bytes: int = 0):
+        self.lib = _lib.load()
+        self.device = torch.device(device if device is not None else "cuda", )
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        h = ctypes.c_void_p()
+        st = self.lib.muon_create(self.device.index, int(workspace_bytes), ctypes.byref(h))
+        if st != _lib.MUON_OK:
+            raise MuonError(st, "muon_create")
+        self.handle = h
+        self.workspace_bytes = int(workspace_bytes)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            self.lib.muon_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _raise(self, st: int, what: str):
+        if st != _lib.MUON_OK:
+            raise MuonError(st, f"{what}: {self.lib.muon_last_error(self.handle).decode()}")
+
+    # -- the three steps ----------------------------------------------------
+    def momentum_update(self, grad: torch.Tensor, momentum: torch.Tensor, update_out: torch.Tensor,
+                        beta: float = 0.95, nesterov: bool = True, stream=None):
+        for t, n in ((grad, "grad"), (momentum, "momentum"), (update_out, "update_out")):
+            _check(t, n, self.device)
+        if momentum.dtype != torch.float32:
+            raise TypeError("momentum must be float32")
+        numel = grad.numel()
+        if momentum.numel() != numel or update_out.numel() != numel:
+            raise ValueError("grad, momentum and update_out must have the same numel")
+        st = self.lib.muon_momentum_update(
+            self.handle, _stream(self.device, stream), ctypes.c_void_p(grad.data_ptr()), _dtype(grad),
+            ctypes.c_void_p(momentum.data_ptr()), ctypes.c_void_p(update_out.data_ptr()),
+            _dtype(update_out), numel, float(beta), 1 if nesterov else 0)
+        self._raise(st, "muon_momentum_update")
+
+    def newton_schulz(self, mats: Sequence[torch.Tensor], out: Optional[Sequence[torch.Tensor]] = None,
+                      head_rows: int = 0, params: Optional[NsParams] = None,
+                      nonfinite_flag: Optional[torch.Tensor] = None, stream=None,
+                      _ptrs: Optional[Tuple] = None):
+        """Orthogonalise a same-shape group of matrices (in place when out is None)."""
+        if params is None:
+            params = ns_params(compute="bf16" if mats[0].dtype == torch.bfloat16 else "f32")
+        if _ptrs is None:
+            _ptrs = self.pointer_arrays(mats, out)
+        rows, cols = mats[0].shape[-2], mats[0].shape[-1]
+        flag = ctypes.c_void_p(nonfinite_flag.data_ptr()) if nonfinite_flag is not None else None
+        pin, pout, count = _ptrs
+        st = self.lib.muon_newton_schulz_batched(
+            self.handle, _stream(self.device, stream), pin, count, Shape(rows, cols, head_rows),
+            _dtype(mats[0]), ctypes.byref(params), pout, flag)
+        self._raise(st, "muon_newton_schulz_batched")
+
+    def pointer_arrays(self, mats: Sequence[torch.Tensor], out: Optional[Sequence[torch.Tensor]] = None):
+        """Host pointer arrays for newton_schulz (cacheable while the tensors live)."""
+        if isinstance(mats, torch.Tensor) and mats.dim() == 3:
+            mats = list(mats.unbind(0))
+        if out is not None and isinstance(out, torch.Tensor) and out.dim() == 3:
+            out = list(out.unbind(0))
+        shape, dt = mats[0].shape, mats[0].dtype
+        for i, m in enumerate(mats):
+            _check(m, f"mats[{i}]", self.device)
+            if m.dim() != 2 or m.shape != shape or m.dtype != dt:
+                raise ValueError("all matrices of one call must be 2D with one shape and dtype")
+        arr_t = ctypes.c_void_p * len(mats)
+        pin = arr_t(*[m.data_ptr() for m in mats])
+        pout = None
+        if out is not None:
+            if len(out) != len(mats):
+                raise ValueError("out must have one matrix per input")
+            for i, o in enumerate(out):
+                _check(o, f"out[{i}]", self.device)
+                if o.shape != shape or o.dtype != dt:
+                    raise ValueError("out matrices must match the inputs")
+            pout = arr_t(*[o.data_ptr() for o in out])
+        return pin, pout, len(mats)
+
+    def apply(self, master: torch.Tensor, update: torch.Tensor, lr: float, scale: float = 1.0,
+              weight_decay: float = 0.0, weight_bf16: Optional[torch.Tensor] = None, stream=None):
+        _check(master, "master", self.device)
+        _check(update, "update", self.device)
+        if master.dtype != torch.float32:
+            raise TypeError("master must be float32")
+        numel = master.numel()
+        if update.numel() != numel:
+            raise ValueError("master and update must have the same numel")
+        wb = None
+        if weight_bf16 is not None:
+            _check(weight_bf16, "weight_bf16", self.device)
+            if weight_bf16.dtype != torch.bfloat16 or weight_bf16.numel() != numel:
+                raise ValueError("weight_bf16 must be bfloat16 with the master's numel")
+            wb = ctypes.c_void_p(weight_bf16.data_ptr())
+        st = self.lib.muon_apply(self.handle, _stream(self.device, stream),
+                                 ctypes.c_void_p(master.data_ptr()), ctypes.c_void_p(update.data_ptr()),
+                                 _dtype(update), wb, numel, float(lr), float(scale), float(weight_decay))
+        self._raise(st, "muon_apply")
+
+    # -- timing ---------------------------------------------------------------
+    def timing_enable(self, enable: bool = True, capacity: int = 8192):
+        self._raise(self.lib.muon_timing_enable(self.handle, 1 if enable else 0, capacity), "timing_enable")
+
+    def timing_reset(self):
+        self._raise(self.lib.muon_timing_reset(self.handle), "timing_reset")
+
+    def timing_read(self) -> dict:
+        res = {}
+        for k, name in enumerate(_lib.KERNEL_CLASSES):
+            ms, n = ctypes.c_double(), ctypes.c_int64()
+            self._raise(self.lib.muon_timing_read(self.handle, k, ctypes.byref(ms), ctypes.byref(n)),
+                        "timing_read")
+            res[name] = (ms.value, n.value)
+        return res
+
+
+@dataclass
+class BucketInfo:
+    m: int
+    n: int
+    count: int
+    units: int
+    numel: int
+    full_bytes: int
+    workspace_bytes: int
+    over_cap: bool
+    shape_groups: int
+    indices: List[int]
+
+
+class Plan:
+    """Host scheduler result: micro-buckets of whole matrices under a cap."""
+
+    def __init__(self, shapes: Sequence[Tuple[int, int, int]], cap_bytes: int, cap_kind: str = "full",
+                 compute: str = "bf16"):
+        lib = _lib.load()
+        arr = (Shape * len(shapes))(*[Shape(r, c, h) for (r, c, h) in shapes])
+        h = ctypes.c_void_p()
+        kind = MUON_CAP_FULL_BYTES if cap_kind == "full" else MUON_CAP_WORKSPACE
+        st = lib.muon_plan_create(arr, len(shapes), int(cap_bytes), kind,
+                                  MUON_BF16 if compute == "bf16" else MUON_F32, ctypes.byref(h))
+        if st != _lib.MUON_OK:
+            raise MuonError(st, "muon_plan_create")
+        try:
+            self.buckets: List[BucketInfo] = []
+            for b in range(lib.muon_plan_num_buckets(h)):
+                info = _lib.BucketInfo()
+                lib.muon_plan_bucket(h, b, ctypes.byref(info), None)
+                idx = (ctypes.c_int64 * info.count)()
+                lib.muon_plan_bucket(h, b, ctypes.byref(info), idx)
+                self.buckets.append(BucketInfo(info.m, info.n, info.count, info.units, info.numel,
+                                               info.full_bytes, info.workspace_bytes,
+                                               bool(info.over_cap), info.shape_groups, list(idx)))
+            self.max_workspace = int(lib.muon_plan_max_workspace(h))
+        finally:
+            lib.muon_plan_destroy(h)

@@ -1,0 +1,507 @@
+// libmuon C ABI: context, argument validation and the Newton-Schulz driver.
+//
+// The driver enqueues, per batched call: the deterministic norm reduction,
+// then `steps` times Gram -> symmetric square -> update, all on the caller's
+// stream, with no host synchronisation and no device allocation (blog "Muon
+// Optimizer + FSDP", section "Memory control", item 2: one preallocated
+// workspace, only views per micro-bucket).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "muon.h"
+#include "muon_internal.h"
+#include "ns_layout.h"
+
+namespace {
+
+constexpr int kTabSlots = 4;
+constexpr int64_t kTabCap = 65536;  // pointers per table (per in/out) per slot
+
+struct DeviceGuard {
+  int prev = -1;
+  bool ok = false;
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    ok = hipSetDevice(dev) == hipSuccess;
+  }
+  ~DeviceGuard() {
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+}  // namespace
+
+struct muon_ctx {
+  int device = 0;
+  int cus = 256;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  uint64_t* host_tab = nullptr;  // pinned staging, kTabSlots * 2 * kTabCap
+  uint64_t* dev_tab = nullptr;   // device tables, same layout
+  hipEvent_t tab_ev[kTabSlots] = {};
+  bool tab_used[kTabSlots] = {};
+  int tab_next = 0;
+  // timing
+  bool timing = false;
+  std::vector<hipEvent_t> tev;
+  std::vector<int> tcls;
+  size_t tused = 0;  // events recorded (pairs * 2)
+  std::string err;
+};
+
+namespace {
+
+muon_status_t fail(muon_ctx* c, muon_status_t s, const char* what) {
+  if (c) c->err = what;
+  return s;
+}
+
+muon_status_t hip_fail(muon_ctx* c, hipError_t e, const char* where) {
+  if (c) {
+    c->err = std::string(where) + ": " + hipGetErrorString(e);
+  }
+  return MUON_EHIP;
+}
+
+// Record the start event of a timed launch; returns the pair index or -1.
+long tstart(muon_ctx* c, hipStream_t s, int cls) {
+  if (!c->timing || c->tused + 2 > c->tev.size()) return -1;
+  const long k = static_cast<long>(c->tused);
+  if (hipEventRecord(c->tev[k], s) != hipSuccess) return -1;
+  c->tcls[k / 2] = cls;
+  return k;
+}
+void tstop(muon_ctx* c, hipStream_t s, long k) {
+  if (k < 0) return;
+  if (hipEventRecord(c->tev[k + 1], s) == hipSuccess) c->tused = static_cast<size_t>(k) + 2;
+}
+
+bool is_dtype(int32_t d) { return d == MUON_F32 || d == MUON_BF16; }
+size_t esize(int32_t d) { return d == MUON_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* muon_status_string(muon_status_t s) {
+  switch (s) {
+    case MUON_OK: return "ok";
+    case MUON_EINVAL: return "invalid argument";
+    case MUON_ESHAPE: return "invalid shape";
+    case MUON_EDTYPE: return "unsupported dtype";
+    case MUON_EWORKSPACE: return "workspace too small";
+    case MUON_EHIP: return "HIP runtime error";
+    case MUON_ENOMEM: return "out of host memory";
+  }
+  return "unknown status";
+}
+
+const char* muon_last_error(const muon_ctx_t* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+void muon_ns_params_default(muon_ns_params_t* p) {
+  if (!p) return;
+  p->steps = 5;
+  p->a = 3.4445f;
+  p->b = -4.7750f;
+  p->c = 2.0315f;
+  p->eps = 1e-7f;
+  p->compute = MUON_BF16;
+}
+
+size_t muon_ctx_workspace_bytes(const muon_ctx_t* ctx) { return ctx ? ctx->ws_bytes : 0; }
+
+muon_status_t muon_create(int device, size_t workspace_bytes, muon_ctx_t** out) {
+  if (out == nullptr) return MUON_EINVAL;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return MUON_EHIP;
+  DeviceGuard g(device);
+  if (!g.ok) return MUON_EHIP;
+  muon_ctx* c = new (std::nothrow) muon_ctx;
+  if (c == nullptr) return MUON_ENOMEM;
+  c->device = device;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) == hipSuccess &&
+      cus > 0)
+    c->cus = cus;
+  const size_t tab_bytes = sizeof(uint64_t) * kTabSlots * 2 * kTabCap;
+  bool ok = hipMalloc(reinterpret_cast<void**>(&c->ws), std::max<size_t>(workspace_bytes, 256)) ==
+            hipSuccess;
+  ok = ok && hipMalloc(reinterpret_cast<void**>(&c->dev_tab), tab_bytes) == hipSuccess;
+  ok = ok && hipHostMalloc(reinterpret_cast<void**>(&c->host_tab), tab_bytes, 0) == hipSuccess;
+  for (int i = 0; ok && i < kTabSlots; ++i)
+    ok = hipEventCreateWithFlags(&c->tab_ev[i], hipEventDisableTiming) == hipSuccess;
+  if (!ok) {
+    (void)hipGetLastError();
+    muon_destroy(c);
+    return MUON_EHIP;
+  }
+  c->ws_bytes = workspace_bytes;
+  *out = c;
+  return MUON_OK;
+}
+
+muon_status_t muon_destroy(muon_ctx_t* c) {
+  if (c == nullptr) return MUON_OK;
+  DeviceGuard g(c->device);
+  (void)hipDeviceSynchronize();
+  for (auto& e : c->tev) (void)hipEventDestroy(e);
+  for (int i = 0; i < kTabSlots; ++i)
+    if (c->tab_ev[i]) (void)hipEventDestroy(c->tab_ev[i]);
+  if (c->host_tab) (void)hipHostFree(c->host_tab);
+  if (c->dev_tab) (void)hipFree(c->dev_tab);
+  if (c->ws) (void)hipFree(c->ws);
+  delete c;
+  return MUON_OK;
+}
+
+muon_status_t muon_timing_enable(muon_ctx_t* c, int32_t enable, int32_t capacity) {
+  if (c == nullptr || capacity < 0) return MUON_EINVAL;
+  DeviceGuard g(c->device);
+  c->timing = false;
+  if (!enable) return MUON_OK;
+  const size_t want = static_cast<size_t>(capacity > 0 ? capacity : 8192) * 2;
+  try {
+    while (c->tev.size() < want) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return hip_fail(c, hipGetLastError(), "hipEventCreate");
+      c->tev.push_back(e);
+    }
+    c->tcls.assign(c->tev.size() / 2, 0);
+  } catch (...) {
+    return MUON_ENOMEM;
+  }
+  c->tused = 0;
+  c->timing = true;
+  return MUON_OK;
+}
+
+muon_status_t muon_timing_reset(muon_ctx_t* c) {
+  if (c == nullptr) return MUON_EINVAL;
+  c->tused = 0;
+  return MUON_OK;
+}
+
+muon_status_t muon_timing_read(muon_ctx_t* c, int32_t cls, double* total_ms, int64_t* launches) {
+  if (c == nullptr || total_ms == nullptr || launches == nullptr) return MUON_EINVAL;
+  if (cls < 0 || cls >= MUON_K_COUNT) return MUON_EINVAL;
+  DeviceGuard g(c->device);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (size_t k = 0; k + 1 < c->tused; k += 2) {
+    if (c->tcls[k / 2] != cls) continue;
+    hipError_t e = hipEventSynchronize(c->tev[k + 1]);
+    if (e != hipSuccess) return hip_fail(c, e, "hipEventSynchronize");
+    float ms = 0.0f;
+    e = hipEventElapsedTime(&ms, c->tev[k], c->tev[k + 1]);
+    if (e != hipSuccess) return hip_fail(c, e, "hipEventElapsedTime");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return MUON_OK;
+}
+
+muon_status_t muon_momentum_update(muon_ctx_t* c, void* stream, const void* grad,
+                                   int32_t grad_dtype, float* momentum, void* update_out,
+                                   int32_t update_dtype, int64_t numel, float beta,
+                                   int32_t nesterov) {
+  if (c == nullptr) return MUON_EINVAL;
+  if (numel < 0) return fail(c, MUON_EINVAL, "numel < 0");
+  if (!is_dtype(grad_dtype) || !is_dtype(update_dtype)) return fail(c, MUON_EDTYPE, "dtype");
+  if (numel == 0) return MUON_OK;
+  if (!grad || !momentum || !update_out) return fail(c, MUON_EINVAL, "null pointer");
+  if (!(beta >= 0.0f && beta <= 1.0f)) return fail(c, MUON_EINVAL, "beta outside [0, 1]");
+  const size_t nb = static_cast<size_t>(numel);
+  if (ranges_overlap(update_out, nb * esize(update_dtype), grad, nb * esize(grad_dtype)) ||
+      ranges_overlap(update_out, nb * esize(update_dtype), momentum, nb * 4) ||
+      ranges_overlap(grad, nb * esize(grad_dtype), momentum, nb * 4))
+    return fail(c, MUON_EINVAL, "aliasing buffers");
+  if ((reinterpret_cast<uintptr_t>(grad) % esize(grad_dtype)) ||
+      (reinterpret_cast<uintptr_t>(momentum) % 4) ||
+      (reinterpret_cast<uintptr_t>(update_out) % esize(update_dtype)))
+    return fail(c, MUON_EINVAL, "misaligned pointer");
+  DeviceGuard g(c->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float c1 = 1.0f - beta;
+  const long tk = tstart(c, s, MUON_K_MOMENTUM);
+  const hipError_t e = launch_momentum(s, c->cus, grad, grad_dtype, momentum, update_out,
+                                       update_dtype, numel, beta, c1, nesterov ? 1 : 0);
+  tstop(c, s, tk);
+  if (e != hipSuccess) return hip_fail(c, e, "momentum launch");
+  return MUON_OK;
+}
+
+muon_status_t muon_apply(muon_ctx_t* c, void* stream, float* master, const void* update,
+                         int32_t update_dtype, void* weight_bf16, int64_t numel, float lr,
+                         float scale, float weight_decay) {
+  if (c == nullptr) return MUON_EINVAL;
+  if (numel < 0) return fail(c, MUON_EINVAL, "numel < 0");
+  if (!is_dtype(update_dtype)) return fail(c, MUON_EDTYPE, "dtype");
+  if (numel == 0) return MUON_OK;
+  if (!master || !update) return fail(c, MUON_EINVAL, "null pointer");
+  const size_t nb = static_cast<size_t>(numel);
+  if (ranges_overlap(master, nb * 4, update, nb * esize(update_dtype)) ||
+      (weight_bf16 && (ranges_overlap(weight_bf16, nb * 2, master, nb * 4) ||
+                       ranges_overlap(weight_bf16, nb * 2, update, nb * esize(update_dtype)))))
+    return fail(c, MUON_EINVAL, "aliasing buffers");
+  if ((reinterpret_cast<uintptr_t>(master) % 4) ||
+      (reinterpret_cast<uintptr_t>(update) % esize(update_dtype)) ||
+      (weight_bf16 && (reinterpret_cast<uintptr_t>(weight_bf16) % 2)))
+    return fail(c, MUON_EINVAL, "misaligned pointer");
+  DeviceGuard g(c->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float eta = lr * scale;
+  const float decay = 1.0f - lr * weight_decay;
+  const long tk = tstart(c, s, MUON_K_APPLY);
+  const hipError_t e = launch_apply(s, c->cus, master, update, update_dtype, weight_bf16, numel,
+                                    eta, decay, weight_decay != 0.0f ? 1 : 0);
+  tstop(c, s, tk);
+  if (e != hipSuccess) return hip_fail(c, e, "apply launch");
+  return MUON_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Describe `count` matrices (each `per` units of unit_bytes) as a unit-level
+// MatRef: uniform stride when possible, else a device table staged through
+// the pinned ring.  `tab` receives the host-side slot to fill.
+struct UnitsRef {
+  MatRef ref{nullptr, 0, nullptr};
+  bool needs_table = false;
+};
+
+UnitsRef describe(const void* const* p, int64_t count, int64_t per, int64_t unit_bytes) {
+  UnitsRef r;
+  const char* b0 = static_cast<const char*>(p[0]);
+  if (count == 1) {
+    r.ref = MatRef{b0, unit_bytes, nullptr};
+    return r;
+  }
+  const int64_t d = static_cast<const char*>(p[1]) - b0;
+  bool uniform = (per == 1) || (d == per * unit_bytes);
+  for (int64_t i = 2; uniform && i < count; ++i)
+    uniform = (static_cast<const char*>(p[i]) - b0) == i * d;
+  if (uniform) {
+    r.ref = MatRef{b0, per == 1 ? d : unit_bytes, nullptr};
+  } else {
+    r.needs_table = true;
+  }
+  return r;
+}
+
+void fill_table(uint64_t* dst, const void* const* p, int64_t count, int64_t per,
+                int64_t unit_bytes) {
+  for (int64_t i = 0; i < count; ++i)
+    for (int64_t k = 0; k < per; ++k)
+      dst[i * per + k] = reinterpret_cast<uint64_t>(static_cast<const char*>(p[i]) + k * unit_bytes);
+}
+
+int pick_tile(int64_t rows_a, int64_t rows_b) {
+  return (std::min(rows_a, rows_b) >= 256) ? 256 : 128;
+}
+
+}  // namespace
+
+extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
+                                                    const void* const* mats, int64_t count,
+                                                    muon_shape_t shape, int32_t io_dtype,
+                                                    const muon_ns_params_t* prm,
+                                                    void* const* out, int* nonfinite_flag) {
+  if (c == nullptr) return MUON_EINVAL;
+  if (count < 0) return fail(c, MUON_EINVAL, "count < 0");
+  if (prm == nullptr) return fail(c, MUON_EINVAL, "params NULL");
+  if (!is_dtype(io_dtype) || !is_dtype(prm->compute)) return fail(c, MUON_EDTYPE, "dtype");
+  if (io_dtype != prm->compute)
+    return fail(c, MUON_EDTYPE, "io dtype must equal the compute dtype");
+  if (prm->steps < 0 || !(prm->eps >= 0.0f)) return fail(c, MUON_EINVAL, "steps/eps");
+  NsLayout L;
+  if (!ns_layout(shape, count, prm->compute, &L)) return fail(c, MUON_ESHAPE, "shape");
+  if (count == 0) return MUON_OK;
+  if (mats == nullptr) return fail(c, MUON_EINVAL, "mats NULL");
+  const size_t es = esize(io_dtype);
+  for (int64_t i = 0; i < count; ++i) {
+    if (mats[i] == nullptr || (out && out[i] == nullptr)) return fail(c, MUON_EINVAL, "null matrix");
+    if ((reinterpret_cast<uintptr_t>(mats[i]) % es) || (out && reinterpret_cast<uintptr_t>(out[i]) % es))
+      return fail(c, MUON_EINVAL, "misaligned matrix");
+  }
+  if (L.total > c->ws_bytes) return fail(c, MUON_EWORKSPACE, "workspace too small for this call");
+  const int64_t per = L.units / count;
+  const int64_t unit_elems = L.ur * L.uc;
+  const int64_t unit_bytes = unit_elems * static_cast<int64_t>(es);
+  const void* const* outp = out ? reinterpret_cast<const void* const*>(out) : mats;
+
+  UnitsRef in = describe(mats, count, per, unit_bytes);
+  UnitsRef ot = describe(outp, count, per, unit_bytes);
+  if ((in.needs_table || ot.needs_table) && L.units > kTabCap)
+    return fail(c, MUON_EINVAL, "too many irregularly placed units in one call (max 65536)");
+
+  // vector paths need 16-byte aligned units
+  bool al = (unit_bytes % 16) == 0;
+  for (int64_t i = 0; al && i < count; ++i) al = aligned16(mats[i]) && aligned16(outp[i]);
+  const bool mfma = prm->compute == MUON_BF16 && al && (L.ur % 8 == 0) && (L.uc % 8 == 0);
+
+  DeviceGuard g(c->device);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+
+  if (in.needs_table || ot.needs_table) {
+    const int slot = c->tab_next;
+    c->tab_next = (c->tab_next + 1) % kTabSlots;
+    if (c->tab_used[slot]) {
+      e = hipEventSynchronize(c->tab_ev[slot]);
+      if (e != hipSuccess) return hip_fail(c, e, "table slot wait");
+    }
+    uint64_t* hin = c->host_tab + static_cast<size_t>(slot) * 2 * kTabCap;
+    uint64_t* hout = hin + kTabCap;
+    uint64_t* din = c->dev_tab + static_cast<size_t>(slot) * 2 * kTabCap;
+    uint64_t* dout = din + kTabCap;
+    if (in.needs_table) {
+      fill_table(hin, mats, count, per, unit_bytes);
+      e = hipMemcpyAsync(din, hin, sizeof(uint64_t) * L.units, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_fail(c, e, "table upload");
+      in.ref = MatRef{nullptr, 0, din};
+    }
+    if (ot.needs_table) {
+      fill_table(hout, outp, count, per, unit_bytes);
+      e = hipMemcpyAsync(dout, hout, sizeof(uint64_t) * L.units, hipMemcpyHostToDevice, s);
+      if (e != hipSuccess) return hip_fail(c, e, "table upload");
+      ot.ref = MatRef{nullptr, 0, dout};
+    }
+    e = hipEventRecord(c->tab_ev[slot], s);
+    if (e != hipSuccess) return hip_fail(c, e, "table event");
+    c->tab_used[slot] = true;
+  }
+
+  char* ws = c->ws;
+  const int64_t xbytes = L.m * L.n * static_cast<int64_t>(es);
+  const int64_t abytes = L.m * L.m * static_cast<int64_t>(es);
+  const MatRef XA{ws + L.xa, xbytes, nullptr}, XB{ws + L.xb, xbytes, nullptr};
+  const MatRef AR{ws + L.a, abytes, nullptr}, BR{ws + L.b, abytes, nullptr};
+  float* scale = reinterpret_cast<float*>(ws + L.scale);
+  int* zflag = reinterpret_cast<int*>(ws + L.zflag);
+
+  NsNormArgs na;
+  na.in = in.ref;
+  na.unit_elems = unit_elems;
+  na.units = L.units;
+  na.parts = L.parts;
+  na.chunk = L.chunk;
+  na.partial = reinterpret_cast<double*>(ws + L.partial);
+  na.scale = scale;
+  na.zflag = zflag;
+  na.nonfinite = nonfinite_flag;
+  na.eps = prm->eps;
+  long tk = tstart(c, s, MUON_K_NORM);
+  e = launch_norm(s, na, io_dtype == MUON_BF16, al && (unit_elems % 8 == 0));
+  tstop(c, s, tk);
+  if (e != hipSuccess) return hip_fail(c, e, "norm launch");
+
+  const int io_bf16 = io_dtype == MUON_BF16;
+  if (prm->steps == 0) {
+    e = launch_scale_copy(s, in.ref, ot.ref, unit_elems, L.units, scale, io_bf16);
+    return e == hipSuccess ? MUON_OK : hip_fail(c, e, "copy launch");
+  }
+
+  const bool tall = L.ur > L.uc;
+  const int64_t m = L.m, n = L.n;
+  auto gemm = [&](int cls, NsGemmArgs& a, int epi, bool tm, bool tn) -> hipError_t {
+    const int T = mfma ? pick_tile(a.M, a.N) : 64;
+    a.tiles_m = static_cast<int>((a.M + T - 1) / T);
+    a.tiles_n = static_cast<int>((a.N + T - 1) / T);
+    a.tiles_per_unit = (epi == EPI_UPDATE) ? a.tiles_m * a.tiles_n : a.tiles_m * (a.tiles_m + 1) / 2;
+    a.units = L.units;
+    a.zflag = zflag;
+    a.ca = prm->a;
+    a.cb = prm->b;
+    a.cc = prm->c;
+    const long k = tstart(c, s, cls);
+    const hipError_t r = mfma ? launch_ns_gemm_mfma(s, a, epi, tm, tn, T)
+                              : launch_ns_gemm_simple(s, a, epi, tm, tn, io_bf16);
+    tstop(c, s, k);
+    return r;
+  };
+
+  for (int k = 0; k < prm->steps; ++k) {
+    const bool last = (k == prm->steps - 1);
+    const MatRef src = (k == 0) ? in.ref : (((k - 1) % 2 == 0) ? XA : XB);
+    // one-step calls go through XA so the input is never overwritten while read
+    const MatRef dstX = (last && prm->steps > 1) ? ot.ref : ((k % 2 == 0) ? XA : XB);
+
+    NsGemmArgs ga{};
+    ga.pm = src;
+    ga.pn = src;
+    ga.dst = AR;
+    ga.epi = AR;
+    ga.ldm = ga.ldn = tall ? m : n;
+    ga.ldd = ga.lde = m;
+    ga.M = ga.N = static_cast<int>(m);
+    ga.K = static_cast<int>(n);
+    ga.scale = scale;
+    ga.scale_pow = (k == 0) ? 2 : 0;
+    e = gemm(MUON_K_GRAM, ga, EPI_GRAM, tall, tall);
+    if (e != hipSuccess) return hip_fail(c, e, "gram launch");
+
+    NsGemmArgs sa{};
+    sa.pm = AR;
+    sa.pn = AR;
+    sa.dst = BR;
+    sa.epi = AR;
+    sa.ldm = sa.ldn = sa.ldd = sa.lde = m;
+    sa.M = sa.N = sa.K = static_cast<int>(m);
+    sa.scale = nullptr;
+    sa.scale_pow = 0;
+    e = gemm(MUON_K_SYMSQ, sa, EPI_SYMSQ, false, false);
+    if (e != hipSuccess) return hip_fail(c, e, "symsq launch");
+
+    NsGemmArgs ua{};
+    ua.dst = dstX;
+    ua.epi = src;
+    ua.scale = scale;
+    ua.scale_pow = (k == 0) ? 1 : 0;
+    ua.zero_write = last ? 1 : 0;
+    if (!tall) {
+      // X' = a X + B X : rows from B, columns from X (K-major)
+      ua.pm = BR;
+      ua.ldm = m;
+      ua.pn = src;
+      ua.ldn = n;
+      ua.ldd = ua.lde = n;
+      ua.M = static_cast<int>(m);
+      ua.N = static_cast<int>(n);
+    } else {
+      // Y' = a Y + Y B : rows from Y, columns from B (symmetric)
+      ua.pm = src;
+      ua.ldm = m;
+      ua.pn = BR;
+      ua.ldn = m;
+      ua.ldd = ua.lde = m;
+      ua.M = static_cast<int>(n);
+      ua.N = static_cast<int>(m);
+    }
+    ua.K = static_cast<int>(m);
+    e = gemm(MUON_K_UPDATE, ua, EPI_UPDATE, false, !tall);
+    if (e != hipSuccess) return hip_fail(c, e, "update launch");
+  }
+  if (prm->steps == 1) {
+    e = launch_scale_copy(s, XA, ot.ref, unit_elems, L.units, nullptr, io_bf16);
+    if (e != hipSuccess) return hip_fail(c, e, "copy launch");
+  }
+  return MUON_OK;
+}

@@ -1,0 +1,61 @@
+// Device-side helpers shared by the libmuon kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace muon {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+
+// bf16 -> fp32 is exact: the pattern is the high half of the fp32 pattern.
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN;
+// overflow rounds to infinity.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Two fp32 values -> packed pair of bf16 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float load(const float* p) { return *p; }
+  static __device__ __forceinline__ void store(float* p, float v) { *p = v; }
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  static __device__ __forceinline__ void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+}  // namespace muon
+
+// A batch of same-shape matrices on the device: either base + i * stride
+// (bytes) or an explicit device table of pointers.
+struct MatRef {
+  const char* base;
+  int64_t stride;
+  const uint64_t* table;
+};
+
+__host__ __device__ __forceinline__ char* mat_at(const MatRef& r, int64_t i) {
+  return r.table ? reinterpret_cast<char*>(r.table[i]) : const_cast<char*>(r.base) + i * r.stride;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Map the hardware id to a logical id so that each XCD receives one
+// contiguous run of logical tiles: neighbours in logical order share L2.
+__device__ __forceinline__ int64_t xcd_logical_id(int64_t hw, int64_t grid) {
+  const int64_t per = grid / 8, rem = grid % 8;
+  const int64_t x = hw % 8, k = hw / 8;
+  return x * per + (x < rem ? x : rem) + k;
+}

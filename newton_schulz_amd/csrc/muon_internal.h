@@ -1,0 +1,73 @@
+// Host-side declarations of the kernel launchers inside libmuon.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "muon_device.h"
+
+// Epilogue kinds of the Newton-Schulz matrix products.
+enum NsEpi : int {
+  EPI_GRAM = 0,    // A = alpha * (P P^T), upper tiles, mirrored
+  EPI_SYMSQ = 1,   // B = b * A + c * (A A), upper tiles, mirrored
+  EPI_UPDATE = 2   // X' = beta * (a * X + acc), all tiles
+};
+
+// One batched product C = op(P_M) op(P_N)^T over `units` independent units.
+// P_M supplies the rows of C (M of them), P_N its columns (N), K is the
+// contraction length.  trans_m / trans_n: the operand is stored K-major
+// (element (r, k) at k * ld + r) instead of row-major (r * ld + k).
+struct NsGemmArgs {
+  MatRef pm, pn, dst, epi;
+  int64_t ldm, ldn, ldd, lde;  // leading dimensions in elements
+  int M, N, K;
+  int tiles_m, tiles_n, tiles_per_unit;
+  int64_t units;
+  const float* scale;  // per-unit normalisation factor s, or nullptr
+  int scale_pow;       // 0: not applied, 1: multiply by s, 2: by s*s
+  const int* zflag;    // per-unit "norm is zero" flag, or nullptr
+  int zero_write;      // EPI_UPDATE: write zeros for zero units (last iteration)
+  float ca, cb, cc;    // quintic coefficients a, b, c
+};
+
+struct NsNormArgs {
+  MatRef in;
+  int64_t unit_elems;
+  int64_t units;
+  int parts;           // partial sums per unit
+  int64_t chunk;       // elements per partial (multiple of 8)
+  double* partial;     // [units][parts]
+  float* scale;        // [units] : 1 / (||Y||_F + eps)
+  int* zflag;          // [units] : ||Y||_F == 0
+  int* nonfinite;      // device flag or nullptr
+  float eps;
+};
+
+hipError_t launch_momentum(hipStream_t s, int cus, const void* grad, int gdt, float* mom,
+                           void* upd, int udt, int64_t numel, float beta, float c1,
+                           int nesterov);
+hipError_t launch_apply(hipStream_t s, int cus, float* master, const void* upd, int udt,
+                        void* wbf, int64_t numel, float eta, float decay, int has_wd);
+
+hipError_t launch_norm(hipStream_t s, const NsNormArgs& a, int io_bf16, bool vec);
+// out[u] = s[u] * in[u], element-wise over units of unit_elems (steps == 0, copies).
+hipError_t launch_scale_copy(hipStream_t s, MatRef in, MatRef out, int64_t unit_elems,
+                             int64_t units, const float* scale, int io_bf16);
+
+// bf16 MFMA path (all of M, N, K, leading dims multiples of 8; 16-byte aligned bases).
+// tile: 128 or 256.  Returns hipErrorInvalidValue for an unsupported combination.
+hipError_t launch_ns_gemm_mfma(hipStream_t s, const NsGemmArgs& a, int epi, bool trans_m,
+                               bool trans_n, int tile);
+// Generic path (any sizes; fp32 or bf16 storage, fp32 FMA accumulation).
+hipError_t launch_ns_gemm_simple(hipStream_t s, const NsGemmArgs& a, int epi, bool trans_m,
+                                 bool trans_n, int io_bf16);
+
+// Tile bookkeeping shared by host and device.
+__host__ __device__ __forceinline__ void upper_tile(int t, int& ti, int& tj) {
+  // Column-wise enumeration of the upper triangle: t = tj*(tj+1)/2 + ti, ti <= tj.
+  int j = static_cast<int>((sqrtf(8.0f * static_cast<float>(t) + 1.0f) - 1.0f) * 0.5f);
+  while (j * (j + 1) / 2 > t) --j;
+  while ((j + 1) * (j + 2) / 2 <= t) ++j;
+  tj = j;
+  ti = t - j * (j + 1) / 2;
+}

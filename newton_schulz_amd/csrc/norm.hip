@@ -1,0 +1,151 @@
+// Frobenius norm of every Newton-Schulz unit, reduced deterministically.
+//
+// X_0 = Y / (||Y||_F + eps) starts the iteration; the blog "Muon Optimizer +
+// FSDP" (section "Memory control", item 4) advises keeping the normalisation
+// scalars in FP32 even when the buffers are BF16.  Here the squares are formed
+// exactly (bf16^2 fits fp32; fp32^2 fits fp64) and summed in fp64 in a fixed
+// order: per thread strided, then a fixed shared-memory tree, then the parts
+// of a unit in index order.  No atomics take part in the sum, so the scale is
+// bit-reproducible.  The scale 1/(||Y|| + eps) is folded into the first
+// iteration's epilogues instead of rewriting Y.
+#include "muon_device.h"
+#include "muon_internal.h"
+
+using muon::bf16_t;
+
+namespace {
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(256) void norm_partial_kernel(NsNormArgs a) {
+  const int64_t u = blockIdx.y;
+  const int p = blockIdx.x;
+  const T* base = reinterpret_cast<const T*>(mat_at(a.in, u));
+  const int64_t start = static_cast<int64_t>(p) * a.chunk;
+  int64_t end = start + a.chunk;
+  if (end > a.unit_elems) end = a.unit_elems;
+  double acc = 0.0;
+  if (VEC) {
+    // start is a multiple of 8; full 8-element groups first
+    const int64_t nfull = (end > start) ? (end - start) / 8 : 0;
+    for (int64_t g = threadIdx.x; g < nfull; g += 256) {
+      const int64_t e = start + 8 * g;
+      if (sizeof(T) == 2) {
+        const uint4 v = *reinterpret_cast<const uint4*>(base + e);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        double d = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+          d += static_cast<double>(lo * lo);
+          d += static_cast<double>(hi * hi);
+        }
+        acc += d;
+      } else {
+        const float4* q = reinterpret_cast<const float4*>(base + e);
+        const float4 x = q[0], y = q[1];
+        const float v[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
+        double d = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) d += static_cast<double>(v[i]) * static_cast<double>(v[i]);
+        acc += d;
+      }
+    }
+    for (int64_t e = start + 8 * nfull + threadIdx.x; e < end; e += 256) {
+      const double v = static_cast<double>(muon::Elem<T>::load(base + e));
+      acc += v * v;
+    }
+  } else {
+    for (int64_t e = start + threadIdx.x; e < end; e += 256) {
+      const double v = static_cast<double>(muon::Elem<T>::load(base + e));
+      acc += v * v;
+    }
+  }
+  __shared__ double red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) a.partial[u * a.parts + p] = red[0];
+}
+
+__global__ __launch_bounds__(256) void norm_finalize_kernel(NsNormArgs a) {
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (u >= a.units) return;
+  double s = 0.0;
+  for (int p = 0; p < a.parts; ++p) s += a.partial[u * a.parts + p];
+  const double nrm = sqrt(s);
+  a.scale[u] = static_cast<float>(1.0 / (nrm + static_cast<double>(a.eps)));
+  a.zflag[u] = (s == 0.0) ? 1 : 0;
+  if (a.nonfinite && !isfinite(s)) atomicOr(a.nonfinite, 1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void scale_copy_kernel(MatRef in, MatRef out, int64_t n,
+                                                         const float* scale) {
+  const int64_t u = blockIdx.y;
+  const T* src = reinterpret_cast<const T*>(mat_at(in, u));
+  T* dst = reinterpret_cast<T*>(mat_at(out, u));
+  const float s = scale ? scale[u] : 1.0f;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    muon::Elem<T>::store(dst + e, s * muon::Elem<T>::load(src + e));
+  }
+}
+
+}  // namespace
+
+// MatRef of units [u0, ...) of r.
+static MatRef shifted(MatRef r, int64_t u0) {
+  if (r.table) r.table += u0;
+  else r.base += u0 * r.stride;
+  return r;
+}
+
+hipError_t launch_norm(hipStream_t s, const NsNormArgs& a, int io_bf16, bool vec) {
+  if (a.units == 0) return hipSuccess;
+  constexpr int64_t kMaxY = 65535;
+  for (int64_t u0 = 0; u0 < a.units; u0 += kMaxY) {
+    NsNormArgs c = a;
+    c.units = (a.units - u0 < kMaxY) ? a.units - u0 : kMaxY;
+    c.in = shifted(a.in, u0);
+    c.partial = a.partial + u0 * a.parts;
+    c.scale = a.scale + u0;
+    c.zflag = a.zflag + u0;
+    dim3 grid(static_cast<unsigned>(c.parts), static_cast<unsigned>(c.units));
+    if (io_bf16) {
+      if (vec) norm_partial_kernel<bf16_t, true><<<grid, 256, 0, s>>>(c);
+      else norm_partial_kernel<bf16_t, false><<<grid, 256, 0, s>>>(c);
+    } else {
+      if (vec) norm_partial_kernel<float, true><<<grid, 256, 0, s>>>(c);
+      else norm_partial_kernel<float, false><<<grid, 256, 0, s>>>(c);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    norm_finalize_kernel<<<static_cast<unsigned>((c.units + 255) / 256), 256, 0, s>>>(c);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_scale_copy(hipStream_t s, MatRef in, MatRef out, int64_t unit_elems,
+                             int64_t units, const float* scale, int io_bf16) {
+  if (units == 0 || unit_elems == 0) return hipSuccess;
+  int64_t bx = (unit_elems + 255) / 256;
+  if (bx > 1024) bx = 1024;
+  constexpr int64_t kMaxY = 65535;
+  for (int64_t u0 = 0; u0 < units; u0 += kMaxY) {
+    const int64_t n = (units - u0 < kMaxY) ? units - u0 : kMaxY;
+    dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(n));
+    const MatRef i0 = shifted(in, u0), o0 = shifted(out, u0);
+    const float* s0 = scale ? scale + u0 : nullptr;
+    if (io_bf16) scale_copy_kernel<bf16_t><<<grid, 256, 0, s>>>(i0, o0, unit_elems, s0);
+    else scale_copy_kernel<float><<<grid, 256, 0, s>>>(i0, o0, unit_elems, s0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}

@@ -1,0 +1,203 @@
+// Host scheduler: same-shape buckets cut into micro-buckets under a cap.
+//
+// The blog "Muon Optimizer + FSDP" recommends processing XTuner-style same-
+// shape buckets (introduction; section "Chunked communication") in micro-
+// buckets of whole matrices under a dedicated Muon cap (section "Memory
+// control", item 1, estimate_muon_peak(bucket) <= workspace cap), merging
+// same-shape matrices across layers (item 6) and planning buffer addresses
+// once (section "DBuffer").  Pure host code, no HIP calls.
+#include <algorithm>
+#include <map>
+#include <new>
+#include <utility>
+#include <vector>
+
+#include "muon.h"
+#include "ns_layout.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+// Shared with muon_api.hip, so the reported size and the carve-up agree.
+bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* L) {
+  if (s.rows <= 0 || s.cols <= 0 || s.head_rows < 0 || count < 0) return false;
+  if (s.head_rows > 0 && s.rows % s.head_rows != 0) return false;
+  if (compute != MUON_BF16 && compute != MUON_F32) return false;
+  const size_t e = compute == MUON_BF16 ? 2 : 4;
+  NsLayout l;
+  const int64_t per = s.head_rows > 0 ? s.rows / s.head_rows : 1;
+  l.units = count * per;
+  l.ur = s.head_rows > 0 ? s.head_rows : s.rows;
+  l.uc = s.cols;
+  l.m = std::min(l.ur, l.uc);
+  l.n = std::max(l.ur, l.uc);
+  const int64_t ue = l.ur * l.uc;
+  // norm partial sums: about 32K elements per part, at most 512 parts
+  int64_t parts = (ue + 32767) / 32768;
+  if (parts < 1) parts = 1;
+  if (parts > 512) parts = 512;
+  int64_t chunk = (ue + parts - 1) / parts;
+  chunk = (chunk + 7) / 8 * 8;
+  parts = (ue + chunk - 1) / chunk;
+  l.parts = static_cast<int>(parts);
+  l.chunk = chunk;
+  const size_t U = static_cast<size_t>(l.units);
+  const size_t xbytes = align_up(U * static_cast<size_t>(l.m * l.n) * e);
+  const size_t abytes = align_up(U * static_cast<size_t>(l.m * l.m) * e);
+  size_t off = 0;
+  l.xa = off; off += xbytes;
+  l.xb = off; off += xbytes;
+  l.a = off; off += abytes;
+  l.b = off; off += abytes;
+  l.scale = off; off += align_up(U * 4);
+  l.zflag = off; off += align_up(U * 4);
+  l.partial = off; off += align_up(U * static_cast<size_t>(l.parts) * 8);
+  l.total = count == 0 ? 0 : off;
+  *L = l;
+  return true;
+}
+
+extern "C" size_t muon_ns_workspace_bytes(muon_shape_t shape, int64_t count, int32_t compute) {
+  NsLayout l;
+  if (!ns_layout(shape, count, compute, &l)) return 0;
+  return l.total;
+}
+
+struct MicroBucket {
+  muon_bucket_info_t info;
+  std::vector<int64_t> idx;
+};
+
+struct muon_plan {
+  std::vector<MicroBucket> buckets;
+  size_t max_ws = 0;
+};
+
+static bool same_shape(const muon_shape_t& x, const muon_shape_t& y) {
+  return x.rows == y.rows && x.cols == y.cols && x.head_rows == y.head_rows;
+}
+
+extern "C" muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t count,
+                                          size_t cap_bytes, int32_t cap_kind, int32_t compute,
+                                          muon_plan_t** out) {
+  if (out == nullptr || (count > 0 && shapes == nullptr) || count < 0) return MUON_EINVAL;
+  if (cap_kind != MUON_CAP_FULL_BYTES && cap_kind != MUON_CAP_WORKSPACE) return MUON_EINVAL;
+  if (compute != MUON_BF16 && compute != MUON_F32) return MUON_EDTYPE;
+  *out = nullptr;
+  const size_t e = compute == MUON_BF16 ? 2 : 4;
+  for (int64_t i = 0; i < count; ++i) {
+    NsLayout l;
+    if (!ns_layout(shapes[i], 1, compute, &l)) return MUON_ESHAPE;
+  }
+  muon_plan* plan = new (std::nothrow) muon_plan;
+  if (plan == nullptr) return MUON_ENOMEM;
+  try {
+    // buckets by canonical unit shape, in order of first appearance
+    std::vector<std::pair<int64_t, int64_t>> keys;
+    std::map<std::pair<int64_t, int64_t>, size_t> key_id;
+    std::vector<std::vector<int64_t>> members;
+    for (int64_t i = 0; i < count; ++i) {
+      const muon_shape_t& s = shapes[i];
+      const int64_t ur = s.head_rows > 0 ? s.head_rows : s.rows;
+      const std::pair<int64_t, int64_t> k(std::min(ur, s.cols), std::max(ur, s.cols));
+      auto it = key_id.find(k);
+      if (it == key_id.end()) {
+        key_id[k] = keys.size();
+        keys.push_back(k);
+        members.emplace_back();
+        it = key_id.find(k);
+      }
+      members[it->second].push_back(i);
+    }
+    for (size_t b = 0; b < keys.size(); ++b) {
+      // order members by exact shape, shapes in order of first appearance
+      std::vector<muon_shape_t> order;
+      for (int64_t i : members[b]) {
+        bool seen = false;
+        for (const auto& o : order) seen = seen || same_shape(o, shapes[i]);
+        if (!seen) order.push_back(shapes[i]);
+      }
+      std::vector<int64_t> sorted;
+      for (const auto& o : order)
+        for (int64_t i : members[b])
+          if (same_shape(o, shapes[i])) sorted.push_back(i);
+
+      auto cost = [&](int64_t i) -> size_t {
+        const muon_shape_t& s = shapes[i];
+        return cap_kind == MUON_CAP_FULL_BYTES
+                   ? e * static_cast<size_t>(s.rows * s.cols)
+                   : muon_ns_workspace_bytes(s, 1, compute);
+      };
+      std::vector<int64_t> cur;
+      size_t cur_cost = 0;
+      auto flush = [&]() {
+        if (cur.empty()) return;
+        MicroBucket mb;
+        mb.idx = cur;
+        muon_bucket_info_t& in = mb.info;
+        in.m = keys[b].first;
+        in.n = keys[b].second;
+        in.count = static_cast<int64_t>(cur.size());
+        in.units = 0;
+        in.numel = 0;
+        in.workspace_bytes = 0;
+        in.shape_groups = 0;
+        in.over_cap = (cur.size() == 1 && cur_cost > cap_bytes) ? 1 : 0;
+        size_t r = 0;
+        while (r < cur.size()) {
+          size_t q = r;
+          while (q < cur.size() && same_shape(shapes[cur[q]], shapes[cur[r]])) ++q;
+          const muon_shape_t& s = shapes[cur[r]];
+          const int64_t run = static_cast<int64_t>(q - r);
+          in.units += run * (s.head_rows > 0 ? s.rows / s.head_rows : 1);
+          in.numel += run * s.rows * s.cols;
+          in.workspace_bytes += muon_ns_workspace_bytes(s, run, compute);
+          in.shape_groups += 1;
+          r = q;
+        }
+        in.full_bytes = e * static_cast<size_t>(in.numel);
+        plan->max_ws = std::max(plan->max_ws, in.workspace_bytes);
+        plan->buckets.push_back(std::move(mb));
+        cur.clear();
+        cur_cost = 0;
+      };
+      for (int64_t i : sorted) {
+        const size_t c = cost(i);
+        if (!cur.empty() && cur_cost + c > cap_bytes) flush();
+        cur.push_back(i);
+        cur_cost += c;
+      }
+      flush();
+    }
+  } catch (...) {
+    delete plan;
+    return MUON_ENOMEM;
+  }
+  *out = plan;
+  return MUON_OK;
+}
+
+extern "C" int64_t muon_plan_num_buckets(const muon_plan_t* plan) {
+  return plan ? static_cast<int64_t>(plan->buckets.size()) : 0;
+}
+
+extern "C" muon_status_t muon_plan_bucket(const muon_plan_t* plan, int64_t b,
+                                          muon_bucket_info_t* info, int64_t* indices) {
+  if (plan == nullptr || info == nullptr) return MUON_EINVAL;
+  if (b < 0 || b >= static_cast<int64_t>(plan->buckets.size())) return MUON_EINVAL;
+  const MicroBucket& mb = plan->buckets[static_cast<size_t>(b)];
+  *info = mb.info;
+  if (indices)
+    for (size_t i = 0; i < mb.idx.size(); ++i) indices[i] = mb.idx[i];
+  return MUON_OK;
+}
+
+extern "C" size_t muon_plan_max_workspace(const muon_plan_t* plan) {
+  return plan ? plan->max_ws : 0;
+}
+
+extern "C" void muon_plan_destroy(muon_plan_t* plan) { delete plan; }

@@ -1,0 +1,101 @@
+"""A whole Muon optimizer step over many matrices, on one device.
+
+State lives in flat device buffers laid out micro-bucket by micro-bucket
+(addresses planned once, views per step: the blog "Muon Optimizer + FSDP",
+sections "Memory control" item 2 and "DBuffer").  Per micro-bucket the step
+enqueues, on one stream and with no host synchronisation:
+    momentum (+ Nesterov) -> batched Newton-Schulz per shape group -> apply
+(the blog's recommended chunked-execution pseudocode, minus the all-to-all
+exchanges, which one device does not need).  The Newton-Schulz input/output
+buffer holds one micro-bucket, so device memory beyond the caller's state is
+cap-bounded: update buffer <= cap (full-byte caps) plus the context
+workspace <= max over micro-buckets of the Newton-Schulz workspace.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Tuple
+
+import torch
+
+from .api import Context, Plan, ns_params
+
+
+class MuonStep:
+    def __init__(self, shapes: Sequence[Tuple[int, int, int]], device=None, lr: float = 0.02,
+                 beta: float = 0.95, nesterov: bool = True, compute: str = "bf16",
+                 grad_dtype: torch.dtype = torch.bfloat16, cap_bytes: int = 512 << 20,
+                 cap_kind: str = "full", ns_steps: int = 5, keep_bf16_weights: bool = False,
+                 weight_decay: float = 0.0, scale: float = 1.0):
+        self.device = torch.device(device if device is not None else "cuda")
+        if self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
+        self.shapes = [tuple(s) for s in shapes]
+        self.lr, self.beta, self.nesterov = lr, beta, nesterov
+        self.weight_decay, self.scale = weight_decay, scale
+        self.compute = compute
+        self.cdtype = torch.bfloat16 if compute == "bf16" else torch.float32
+        self.params = ns_params(steps=ns_steps, compute=compute)
+        self.plan = Plan(self.shapes, cap_bytes, cap_kind, compute)
+
+        # flat layout: matrices in plan order
+        self.order: List[int] = [i for b in self.plan.buckets for i in b.indices]
+        self.offset = [0] * len(self.shapes)
+        off = 0
+        for i in self.order:
+            self.offset[i] = off
+            r, c, _ = self.shapes[i]
+            off += r * c
+        self.numel = off
+        dev = self.device
+        self.grad = torch.zeros(off, dtype=grad_dtype, device=dev)
+        self.momentum = torch.zeros(off, dtype=torch.float32, device=dev)
+        self.master = torch.zeros(off, dtype=torch.float32, device=dev)
+        self.weight_bf16 = torch.zeros(off, dtype=torch.bfloat16, device=dev) if keep_bf16_weights else None
+        max_bucket = max((b.numel for b in self.plan.buckets), default=0)
+        self.update = torch.empty(max(max_bucket, 1), dtype=self.cdtype, device=dev)
+        self.ctx = Context(dev, self.plan.max_workspace)
+
+        # per micro-bucket: element range and shape groups with cached pointer arrays
+        self._work = []
+        pos = 0
+        for b in self.plan.buckets:
+            lo = self.offset[b.indices[0]]
+            hi = lo + b.numel
+            groups = []
+            j = 0
+            while j < len(b.indices):
+                k = j
+                while k < len(b.indices) and self.shapes[b.indices[k]] == self.shapes[b.indices[j]]:
+                    k += 1
+                r, c, h = self.shapes[b.indices[j]]
+                mats = [self._uview(self.offset[i] - lo, r, c) for i in b.indices[j:k]]
+                groups.append((h, mats, self.ctx.pointer_arrays(mats)))
+                j = k
+            self._work.append((lo, hi, groups))
+            pos = hi
+        assert pos == self.numel
+
+    def _uview(self, off: int, r: int, c: int) -> torch.Tensor:
+        return self.update[off:off + r * c].view(r, c)
+
+    def view(self, buf: torch.Tensor, i: int) -> torch.Tensor:
+        """Matrix i of a flat state buffer (grad, momentum, master, weight_bf16)."""
+        r, c, _ = self.shapes[i]
+        return buf[self.offset[i]:self.offset[i] + r * c].view(r, c)
+
+    def momentum_only(self, stream=None):
+        """Momentum update of every matrix, without Newton-Schulz or apply
+        (used to pre-fill momentum); the update output is discarded."""
+        for lo, hi, _ in self._work:
+            self.ctx.momentum_update(self.grad[lo:hi], self.momentum[lo:hi], self.update[:hi - lo],
+                                     self.beta, self.nesterov, stream)
+
+    def step(self, stream=None, nonfinite_flag: Optional[torch.Tensor] = None):
+        for lo, hi, groups in self._work:
+            upd = self.update[:hi - lo]
+            self.ctx.momentum_update(self.grad[lo:hi], self.momentum[lo:hi], upd, self.beta,
+                                     self.nesterov, stream)
+            for h, mats, ptrs in groups:
+                self.ctx.newton_schulz(mats, None, h, self.params, nonfinite_flag, stream, _ptrs=ptrs)
+            wb = self.weight_bf16[lo:hi] if self.weight_bf16 is not None else None
+            self.ctx.apply(self.master[lo:hi], upd, self.lr, self.scale, self.weight_decay, wb, stream)

@@ -1,0 +1,154 @@
+"""The C ABI without a GPU: exports, host scheduler, workspace arithmetic,
+argument validation.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from newton_schulz_amd import _lib
+from newton_schulz_amd.api import Plan, ns_workspace_bytes
+from newton_schulz_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    # symbols are exported with C linkage
+    out = os.popen(f"nm -D --defined-only {_lib.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}$", out, flags=re.M), name
+
+
+def test_status_strings():
+    lib = _lib.load()
+    assert lib.muon_status_string(0) == b"ok"
+    assert lib.muon_status_string(4) == b"workspace too small"
+    assert lib.muon_status_string(99) == b"unknown status"
+
+
+def test_create_without_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = _lib.load()
+    h = ctypes.c_void_p()
+    assert lib.muon_create(0, 1 << 20, ctypes.byref(h)) == _lib.MUON_EHIP
+    assert not h.value
+    assert lib.muon_create(0, 0, None) == _lib.MUON_EINVAL
+    assert lib.muon_destroy(None) == _lib.MUON_OK
+
+
+def test_null_context_rejected():
+    lib = _lib.load()
+    p = _lib.NsParams()
+    lib.muon_ns_params_default(ctypes.byref(p))
+    assert (p.steps, round(p.a, 4), round(p.b, 4), round(p.c, 4), p.compute) == (5, 3.4445, -4.775, 2.0315, 1)
+    assert lib.muon_momentum_update(None, None, None, 1, None, None, 1, 10, 0.95, 1) == _lib.MUON_EINVAL
+    assert lib.muon_apply(None, None, None, None, 1, None, 10, 0.02, 1.0, 0.0) == _lib.MUON_EINVAL
+    assert lib.muon_newton_schulz_batched(None, None, None, 1, _lib.Shape(8, 8, 0), 1, ctypes.byref(p),
+                                          None, None) == _lib.MUON_EINVAL
+
+
+def _aligned(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("rows,cols,h,count,compute", [
+    (2560, 4096, 0, 25, "bf16"), (4096, 2560, 0, 3, "bf16"), (128, 2560, 0, 1728, "bf16"),
+    (4096, 2560, 128, 2, "bf16"), (96, 96, 0, 1, "f32"), (256, 64, 0, 2, "f32"),
+])
+def test_workspace_formula(rows, cols, h, count, compute):
+    e = 2 if compute == "bf16" else 4
+    ur = h if h else rows
+    units = count * (rows // ur)
+    m, n = min(ur, cols), max(ur, cols)
+    ue = ur * cols
+    parts = min(max((ue + 32767) // 32768, 1), 512)
+    chunk = -(-ue // parts)
+    chunk = -(-chunk // 8) * 8
+    parts = -(-ue // chunk)
+    want = (2 * _aligned(units * m * n * e) + 2 * _aligned(units * m * m * e)
+            + 2 * _aligned(units * 4) + _aligned(units * parts * 8))
+    assert ns_workspace_bytes(rows, cols, count, h, compute) == want
+    # the stated bound: (2 + 2 m / n) x full bytes, plus small scalars
+    full = units * m * n * e
+    assert want <= (2 + 2 * m / n) * full + 4 * 256 + units * (8 + parts * 8) + 256
+
+
+def test_workspace_rejects_bad_shapes():
+    assert ns_workspace_bytes(100, 64, 1, 30) == 0      # rows % head_rows
+    assert ns_workspace_bytes(0, 64, 1) == 0
+    assert ns_workspace_bytes(64, 64, 0) == 0           # count 0: nothing needed
+
+
+def test_plan_qwen3_4b_buckets():
+    w = synth.qwen3_4b(layers=36)
+    shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
+    plan = Plan(shapes, 512 << 20, "full", "bf16")
+    # canonical buckets (2560,4096): q + o; (1024,2560): k + v; (2560,9728): gate, up, down
+    keys = [(b.m, b.n) for b in plan.buckets]
+    assert keys == [(2560, 4096)] * 3 + [(1024, 2560)] + [(2560, 9728)] * 11
+    assert [b.count for b in plan.buckets] == [25, 25, 22, 72] + [10] * 10 + [8]
+    # every matrix exactly once; each micro-bucket within the cap
+    flat = sorted(i for b in plan.buckets for i in b.indices)
+    assert flat == list(range(len(shapes)))
+    for b in plan.buckets:
+        assert b.full_bytes <= 512 << 20 and not b.over_cap
+        assert b.full_bytes == 2 * sum(shapes[i][0] * shapes[i][1] for i in b.indices)
+    # inside a bucket, same exact shapes are contiguous (q first, then o)
+    first = plan.buckets[0]
+    assert [shapes[i][:2] for i in first.indices] == [(4096, 2560)] * 25
+    assert [shapes[i][:2] for i in plan.buckets[1].indices] == [(4096, 2560)] * 11 + [(2560, 4096)] * 14
+    assert plan.buckets[1].shape_groups == 2 and plan.buckets[2].shape_groups == 1
+    # workspace: stated function of the cap, (2 + 2 m/n) x full bytes at most
+    for b in plan.buckets:
+        scalars = b.units * (8 + 512 * 8) + 8 * 256 * b.shape_groups
+        assert b.workspace_bytes <= (2 + 2 * b.m / b.n) * b.full_bytes + scalars
+    assert plan.max_workspace == max(b.workspace_bytes for b in plan.buckets)
+
+
+def test_plan_workspace_cap_experts():
+    w = synth.qwen3_30b_experts(layers=2)
+    shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
+    plan = Plan(shapes, 1 << 30, "workspace", "bf16")
+    assert all(b.workspace_bytes <= 1 << 30 for b in plan.buckets)
+    assert all((b.m, b.n) == (768, 2048) for b in plan.buckets)
+    assert sum(b.count for b in plan.buckets) == len(shapes)
+    # cross-layer merge: one canonical bucket for all expert matrices
+    assert max(b.count for b in plan.buckets) >= 100
+
+
+def test_plan_over_cap_matrix_alone():
+    plan = Plan([(64, 64, 0), (4096, 4096, 0), (64, 64, 0)], 1 << 20, "full", "bf16")
+    big = [b for b in plan.buckets if b.m == 4096]
+    assert len(big) == 1 and big[0].over_cap and big[0].count == 1
+
+
+def test_plan_per_head_units():
+    plan = Plan([(4096, 2560, 128), (1024, 2560, 128)], 1 << 40, "full", "bf16")
+    assert len(plan.buckets) == 1
+    b = plan.buckets[0]
+    assert (b.m, b.n, b.units, b.shape_groups) == (128, 2560, 32 + 8, 2)
+
+
+def test_plan_rejects_bad_input():
+    from newton_schulz_amd.api import MuonError
+    with pytest.raises(MuonError):
+        Plan([(100, 64, 30)], 1 << 20)
+    with pytest.raises(MuonError):
+        Plan([(0, 64, 0)], 1 << 20)
