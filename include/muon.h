@@ -99,10 +99,9 @@ void muon_ns_params_default(muon_ns_params_t* p);
 /* Workspace one muon_newton_schulz_batched call needs for `count` matrices
  * of `shape` in compute dtype `compute` (pure host function).  Per Newton-
  * Schulz unit of m x n (m = min, n = max of its rows and cols, e = element
- * bytes of the compute dtype): four iterate buffers (X and X^T, ping-pong:
- * 4 e m n) + A and B (2 e m^2) + 8 bytes of scalars + 8 bytes per norm
- * partial (max of ceil(rows/64) ceil(cols/64) and the reduction's parts),
- * each region rounded up to 256 bytes: (4 + 2 m/n) x the unit's e m n bytes
+ * bytes of the compute dtype): two iterate buffers (2 e m n) + A and B
+ * (2 e m^2) + 8 bytes of scalars + 8 bytes per norm partial (at most 512),
+ * each region rounded up to 256 bytes: (2 + 2 m/n) x the unit's e m n bytes
  * plus scalars.  Returns 0 for an invalid shape. */
 size_t muon_ns_workspace_bytes(muon_shape_t shape, int64_t count, int32_t compute);
 

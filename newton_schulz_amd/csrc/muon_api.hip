@@ -390,9 +390,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   const int64_t xbytes = L.m * L.n * static_cast<int64_t>(es);
   const int64_t abytes = L.m * L.m * static_cast<int64_t>(es);
   const MatRef XA{ws + L.xa, xbytes, nullptr}, XB{ws + L.xb, xbytes, nullptr};
-  const MatRef XC{ws + L.xc, xbytes, nullptr}, XD{ws + L.xd, xbytes, nullptr};
   const MatRef AR{ws + L.a, abytes, nullptr}, BR{ws + L.b, abytes, nullptr};
-  const MatRef NONE{nullptr, 0, nullptr};
   float* scale = reinterpret_cast<float*>(ws + L.scale);
   int* zflag = reinterpret_cast<int*>(ws + L.zflag);
   double* partial = reinterpret_cast<double*>(ws + L.partial);
@@ -411,94 +409,9 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     a.cc = prm->c;
   };
 
-  if (mfma) {
-    // Iterates live in two layouts, R (m x n) and T = R^T (n x m); the input
-    // is R when wide and T when tall, and prep writes the other one.
-    // Slots: (XA, XB) = (R, T) of odd iterates, (XC, XD) of even iterates;
-    // the prepped layout of X_0 sits in XC or XD.
-    const MatRef P = tall ? XC : XD;
-    long tk = tstart(c, s, MUON_K_NORM);
-    e = launch_prep(s, in.ref, P, static_cast<int>(L.ur), static_cast<int>(L.uc), L.units, partial,
-                    scale, zflag, nonfinite_flag, prm->eps);
-    tstop(c, s, tk);
-    if (e != hipSuccess) return hip_fail(c, e, "prep launch");
-    if (prm->steps == 0) {
-      e = launch_scale_copy(s, in.ref, ot.ref, unit_elems, L.units, scale, io_bf16);
-      return e == hipSuccess ? MUON_OK : hip_fail(c, e, "copy launch");
-    }
-    for (int k = 0; k < prm->steps; ++k) {
-      const bool last = (k == prm->steps - 1);
-      MatRef R, T;
-      if (k == 0) {
-        R = tall ? P : in.ref;
-        T = tall ? in.ref : P;
-      } else if ((k - 1) % 2 == 0) {
-        R = XA; T = XB;
-      } else {
-        R = XC; T = XD;
-      }
-      const MatRef nR = (k % 2 == 0) ? XA : XC, nT = (k % 2 == 0) ? XB : XD;
-
-      NsGemmArgs ga{};
-      ga.pm = R; ga.pn = R; ga.dst = AR; ga.epi = AR; ga.dst_t = NONE;
-      ga.ldm = ga.ldn = n;
-      ga.ldd = ga.lde = m;
-      ga.M = ga.N = static_cast<int>(m);
-      ga.K = static_cast<int>(n);
-      ga.scale = scale;
-      ga.scale_pow = (k == 0) ? 2 : 0;
-      const int Tg = m >= 256 ? 256 : 128;
-      setup(ga, EPI_GRAM, Tg);
-      tk = tstart(c, s, MUON_K_GRAM);
-      e = launch_ns_gemm_mfma(s, ga, EPI_GRAM, Tg);
-      tstop(c, s, tk);
-      if (e != hipSuccess) return hip_fail(c, e, "gram launch");
-
-      NsGemmArgs sa{};
-      sa.pm = AR; sa.pn = AR; sa.dst = BR; sa.epi = AR; sa.dst_t = NONE;
-      sa.ldm = sa.ldn = sa.ldd = sa.lde = m;
-      sa.M = sa.N = sa.K = static_cast<int>(m);
-      setup(sa, EPI_SYMSQ, Tg);
-      tk = tstart(c, s, MUON_K_SYMSQ);
-      e = launch_ns_gemm_mfma(s, sa, EPI_SYMSQ, Tg);
-      tstop(c, s, tk);
-      if (e != hipSuccess) return hip_fail(c, e, "symsq launch");
-
-      NsGemmArgs ua{};
-      ua.pm = BR; ua.ldm = m;
-      ua.pn = T; ua.ldn = m;
-      ua.epi = R; ua.lde = n;
-      ua.M = static_cast<int>(m);
-      ua.N = static_cast<int>(n);
-      ua.K = static_cast<int>(m);
-      ua.scale = scale;
-      ua.scale_pow = (k == 0) ? 1 : 0;
-      ua.zero_write = last ? 1 : 0;
-      ua.ldd = n;
-      ua.ldt = m;
-      if (last && prm->steps > 1) {
-        ua.dst = tall ? NONE : ot.ref;
-        ua.dst_t = tall ? ot.ref : NONE;
-      } else {
-        ua.dst = nR;
-        ua.dst_t = nT;
-      }
-      const int Tu = m >= 256 ? 256 : 128;
-      setup(ua, EPI_UPDATE, Tu);
-      tk = tstart(c, s, MUON_K_UPDATE);
-      e = launch_ns_gemm_mfma(s, ua, EPI_UPDATE, Tu);
-      tstop(c, s, tk);
-      if (e != hipSuccess) return hip_fail(c, e, "update launch");
-    }
-    if (prm->steps == 1) {
-      e = launch_scale_copy(s, tall ? XB : XA, ot.ref, unit_elems, L.units, nullptr, io_bf16);
-      if (e != hipSuccess) return hip_fail(c, e, "copy launch");
-    }
-    return MUON_OK;
-  }
-
-  // Generic path: deterministic norm, then products with K-major operands
-  // read in place; iterates stay in the input's orientation.
+  // Deterministic norm, then per iteration Gram -> symmetric square ->
+  // update.  Iterates stay in the input's orientation; K-major operands are
+  // read in place (transposed reads), never copied.
   NsNormArgs na;
   na.in = in.ref;
   na.unit_elems = unit_elems;
@@ -519,9 +432,12 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     return e == hipSuccess ? MUON_OK : hip_fail(c, e, "copy launch");
   }
   auto gemm = [&](int cls, NsGemmArgs& a, int epi, bool tm, bool tn) -> hipError_t {
-    setup(a, epi, 64);
+    // 256 x 256 tiles once the smaller output side reaches 256
+    const int T = mfma ? ((std::min(a.M, a.N) >= 256) ? 256 : 128) : 64;
+    setup(a, epi, T);
     const long k = tstart(c, s, cls);
-    const hipError_t r = launch_ns_gemm_simple(s, a, epi, tm, tn, io_bf16);
+    const hipError_t r = mfma ? launch_ns_gemm_mfma(s, a, epi, tm, tn, T)
+                              : launch_ns_gemm_simple(s, a, epi, tm, tn, io_bf16);
     tstop(c, s, k);
     return r;
   };
@@ -532,7 +448,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     const MatRef dstX = (last && prm->steps > 1) ? ot.ref : ((k % 2 == 0) ? XA : XB);
 
     NsGemmArgs ga{};
-    ga.pm = src; ga.pn = src; ga.dst = AR; ga.epi = AR; ga.dst_t = NONE;
+    ga.pm = src; ga.pn = src; ga.dst = AR; ga.epi = AR;
     ga.ldm = ga.ldn = tall ? m : n;
     ga.ldd = ga.lde = m;
     ga.M = ga.N = static_cast<int>(m);
@@ -543,7 +459,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     if (e != hipSuccess) return hip_fail(c, e, "gram launch");
 
     NsGemmArgs sa{};
-    sa.pm = AR; sa.pn = AR; sa.dst = BR; sa.epi = AR; sa.dst_t = NONE;
+    sa.pm = AR; sa.pn = AR; sa.dst = BR; sa.epi = AR;
     sa.ldm = sa.ldn = sa.ldd = sa.lde = m;
     sa.M = sa.N = sa.K = static_cast<int>(m);
     e = gemm(MUON_K_SYMSQ, sa, EPI_SYMSQ, false, false);
@@ -551,7 +467,6 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
 
     NsGemmArgs ua{};
     ua.dst = dstX;
-    ua.dst_t = NONE;
     ua.epi = src;
     ua.scale = scale;
     ua.scale_pow = (k == 0) ? 1 : 0;

@@ -15,13 +15,12 @@ enum NsEpi : int {
 
 // One batched product C = op(P_M) op(P_N)^T over `units` independent units.
 // P_M supplies the rows of C (M of them), P_N its columns (N), K is the
-// contraction length.  The MFMA path reads both operands row-major (element
-// (r, k) at r * ld + k); the generic path also takes trans_m / trans_n
-// (element (r, k) at k * ld + r).  dst receives C row-major; dst_t (update
-// only, may be empty) receives C^T row-major.
+// contraction length.  trans_m / trans_n: the operand is stored K-major
+// (element (r, k) at k * ld + r) instead of K-contiguous (r * ld + k).  dst
+// receives C row-major.
 struct NsGemmArgs {
-  MatRef pm, pn, dst, epi, dst_t;
-  int64_t ldm, ldn, ldd, lde, ldt;  // leading dimensions in elements
+  MatRef pm, pn, dst, epi;
+  int64_t ldm, ldn, ldd, lde;  // leading dimensions in elements
   int M, N, K;
   int tiles_m, tiles_n, tiles_per_unit;
   int64_t units;
@@ -58,12 +57,8 @@ hipError_t launch_scale_copy(hipStream_t s, MatRef in, MatRef out, int64_t unit_
 
 // bf16 MFMA path (all of M, N, K, leading dims multiples of 8; 16-byte aligned
 // bases; each operand smaller than 2 GiB).  tile: 128 or 256.
-hipError_t launch_ns_gemm_mfma(hipStream_t s, const NsGemmArgs& a, int epi, int tile);
-// Transpose each rows x cols bf16 unit of `in` into `outT` (cols x rows) and
-// reduce its squared Frobenius norm: scale = 1 / (||Y|| + eps), zflag, flag.
-int prep_parts(int rows, int cols);
-hipError_t launch_prep(hipStream_t s, MatRef in, MatRef outT, int rows, int cols, int64_t units,
-                       double* partial, float* scale, int* zflag, int* nonfinite, float eps);
+hipError_t launch_ns_gemm_mfma(hipStream_t s, const NsGemmArgs& a, int epi, bool trans_m,
+                               bool trans_n, int tile);
 // Generic path (any sizes; fp32 or bf16 storage, fp32 FMA accumulation).
 hipError_t launch_ns_gemm_simple(hipStream_t s, const NsGemmArgs& a, int epi, bool trans_m,
                                  bool trans_n, int io_bf16);

@@ -1,51 +1,57 @@
 // The three matrix products of one quintic Newton-Schulz iteration on gfx950
 // bf16 matrix cores (v_mfma_f32_32x32x16_bf16, fp32 accumulation).
 //
-// The iterate X (m x n, m <= n) is kept in two layouts: R = X row-major and
-// T = X^T row-major.  With them every product reads both operands along a
-// contiguous K:
-//   gram   A  = alpha X X^T        P_M = P_N = R (K = n); upper tiles, mirrored
-//   symsq  B  = b A + c A A        P_M = P_N = A (A symmetric, so A A = A A^T)
-//   update X' = beta (a X + B X)   P_M = B (K = m), P_N = T (row j of T is
-//                                  column j of X); a X read from R; X' stored
-//                                  as R and/or T
+// Per iteration, with X the m x n iterate (m <= n; a tall matrix Y = X^T is
+// kept in its own orientation):
+//   gram   A  = alpha X X^T      upper-triangle tiles only, mirrored
+//   symsq  B  = b A + c A A      A symmetric, so A A = A A^T; upper tiles
+//   update X' = beta (a X + B X) (tall: Y' = beta (a Y + Y B))
 // alpha = s^2 and beta = s fold the first iteration's normalisation
-// X_0 = s Y (s = 1 / (||Y||_F + eps)) into the products.
+// X_0 = s Y (s = 1 / (||Y||_F + eps)) into the products, so Y is never
+// rewritten.  Every product is C = P_M P_N^T over a contraction index k.  An
+// operand is "K-contiguous" when its rows run along k in memory (X rows for
+// the wide Gram, A, B, Y rows for the tall update) and "K-major" when k is
+// its memory row index (the X operand of the wide update, both Y operands of
+// the tall Gram).  Both kinds are copied into LDS unchanged; K-major tiles
+// are read by the MFMA loop with ds_read_b64_tr_b16, which hands each lane
+// four consecutive k of one column, so no transposed copy of any matrix is
+// ever made.
 //
 // Tiling: BM x BN workgroup tile, BK = 64, 256 threads = 4 waves in 2 x 2,
 // each wave (BM/2) x (BN/2) as 32 x 32 MFMA tiles.  Operand tiles move
-// global -> LDS with buffer_load_dwordx4 ... lds (no registers): each wave
-// instruction fills 8 LDS rows of 128 bytes, lane l writing 16 bytes at
-// 16 l, so each lane fetches the global chunk that the XOR swizzle places
-// there.  Chunks outside the matrix get an offset past the buffer's size and
-// the hardware returns zeros.  Two LDS stages: the loads of stage k+1 are in
-// flight while stage k feeds the MFMAs.  Workgroup ids are remapped so that
-// each XCD (own L2) gets a contiguous run of tiles.
+// global -> LDS with buffer_load_dwordx4 ... lds: each wave instruction
+// fills 1024 contiguous LDS bytes (lane l at 16 l), so every lane fetches the
+// global chunk the XOR swizzle puts at its slot; chunks outside the matrix get
+// an offset past the buffer's size and the hardware returns zeros.  Two LDS
+// stages (the loads of stage k+1 fly while stage k feeds the MFMAs).  The
+// epilogue stages the bf16 tile through LDS so global stores are 16-byte and
+// row-contiguous, and writes the mirror tile of symmetric outputs from
+// transposed LDS reads.  Workgroup ids are remapped so each XCD (own L2)
+// gets a contiguous run of tiles.
 #include "muon_device.h"
 #include "muon_internal.h"
 
+#include <cstdlib>
+#include <cstring>
 #include <utility>
 
 using muon::bf16_t;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr_t;
 
 namespace {
 
-constexpr int BK = 64;                 // bf16 elements of K per stage: one 128-byte LDS row
+constexpr int BK = 64;                 // bf16 elements of K per stage
 constexpr uint32_t kOOB = 0x80000000u; // buffer offset past any matrix: loads return 0
 constexpr int kRsrcWord3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
-__device__ __forceinline__ int lds_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ swz(row)) << 4);
-}
-
 // A pointer every lane holds the same value of, moved to scalar registers
-// (needed for buffer descriptors; a value read from a device table is not
-// known to be uniform otherwise).
+// (buffer descriptors need it; a value read from a device table is not known
+// to be uniform otherwise).
 template <typename T>
 __device__ __forceinline__ T* uniform_ptr(T* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
@@ -59,58 +65,117 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint3
                                            static_cast<int>(bytes), kRsrcWord3);
 }
 
-// Per-lane addressing of one operand tile of R rows (R/8 row groups of 8 LDS
-// rows; wave w issues groups w, w + 4, ...).
+__device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& r, char* lds, uint32_t voff,
+                                      uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+}
+
+// Four consecutive k of one column of a row-major [k][col] LDS tile per lane
+// (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i % 4 of the 8-byte words addressed by lanes i / 4 + 4 r, r = 0..3).
+__device__ __forceinline__ i16x4_t ld_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p));
+}
+
+// ---- K-contiguous operand tile: R rows x BK, 128-byte rows, chunk swizzle
+// (row ^ row >> 3) & 7 keeps the 16 rows an LDS cycle serves on distinct banks.
+__device__ __forceinline__ int rt_off(int row, int chunk) {
+  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+// ---- K-major operand tile: BK rows (k) x R columns, 2R-byte rows, chunk
+// swizzle 4 (k & 3): the four k rows a transposed read touches land on
+// distinct banks.  col is a multiple of 4.
 template <int R>
-struct OperandStream {
-  static constexpr int NG = R / 32;  // row groups per wave
-  uint32_t base[NG];                 // byte offset of this lane's chunk at k = 0, or kOOB
+__device__ __forceinline__ int kt_off(int k, int col) {
+  return k * (2 * R) + (((col >> 3) ^ ((k & 3) << 2)) << 4) + ((col & 7) << 1);
+}
+
+template <int R, bool KMAJOR>
+struct Operand;
+
+template <int R>
+struct Operand<R, false> {
+  static constexpr int NG = R / 32;  // 8 rows per wave instruction, 4 waves
+  uint32_t base[NG];
+  int kc[NG];
   __amdgpu_buffer_rsrc_t rsrc;
 
-  // src: rows x ld bf16 matrix; the tile covers rows [row0, row0 + R).
-  __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int rows, int row0, int wave,
-                                       int lane) {
+  // src: rows x ld matrix; tile rows [row0, row0 + R).
+  __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int rows, int /*K*/,
+                                       int row0, int wave, int lane) {
     rsrc = make_rsrc(src, static_cast<uint32_t>(static_cast<int64_t>(rows) * ld * 2));
-    const int rin = lane >> 3;  // row within the group (0..7)
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
-      const int row = 8 * (wave + 4 * q) + rin;
+      const int row = 8 * (wave + 4 * q) + (lane >> 3);
+      const int lc = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
       const int gr = row0 + row;
-      const int lc = (lane & 7) ^ swz(row);  // logical chunk stored at LDS chunk lane & 7
+      kc[q] = 8 * lc;
       base[q] = (gr < rows) ? static_cast<uint32_t>((static_cast<int64_t>(gr) * ld + 8 * lc) * 2)
                             : kOOB;
     }
   }
-
-  // Issue the loads of K slice [k0, k0 + BK) into the LDS tile at `lds`.
-  __device__ __forceinline__ void issue(char* lds, int k0, int K, int wave, int lane) {
-    const int rin = lane >> 3;
+  __device__ __forceinline__ void issue(char* lds, int k0, int K, int64_t /*ld*/, int wave,
+                                        bool full) const {
+    const uint32_t soff = static_cast<uint32_t>(k0 * 2);
 #pragma unroll
-    for (int q = 0; q < NG; ++q) {
-      const int g = wave + 4 * q;
-      const int row = 8 * g + rin;
-      const int lc = (lane & 7) ^ swz(row);
-      const bool ok = base[q] != kOOB && (k0 + 8 * lc) < K;
-      const uint32_t off = ok ? base[q] + static_cast<uint32_t>(k0 * 2) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_ptr_t)(lds + g * 1024), 16,
-                                               off, 0, 0, 0);
-    }
+    for (int q = 0; q < NG; ++q)
+      dma16(rsrc, lds + (wave + 4 * q) * 1024, (full || k0 + kc[q] < K) ? base[q] : kOOB, soff);
+  }
+  // MFMA operand for tile rows rb .. rb + 31, k = 16 kk + 8 (lane / 32) + 0..7
+  __device__ __forceinline__ bf16x8_t frag(const char* t, int rb, int kk, int lane) const {
+    return *reinterpret_cast<const bf16x8_t*>(t + rt_off(rb + (lane & 31), 2 * kk + (lane >> 5)));
   }
 };
 
-__device__ __forceinline__ void load4_bf16(const bf16_t* p, float v[4]) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(w.x << 16);
-  v[1] = __uint_as_float(w.x & 0xffff0000u);
-  v[2] = __uint_as_float(w.y << 16);
-  v[3] = __uint_as_float(w.y & 0xffff0000u);
-}
+template <int R>
+struct Operand<R, true> {
+  static constexpr int CPR = R / 8;         // 16-byte chunks per tile row
+  static constexpr int RPI = 64 / CPR;      // tile rows per wave instruction
+  static constexpr int NG = BK / RPI / 4;   // instructions per wave
+  uint32_t base[NG];
+  int kr[NG];
+  __amdgpu_buffer_rsrc_t rsrc;
 
-__device__ __forceinline__ void store4_bf16(bf16_t* p, const float v[4]) {
-  uint2 w;
-  w.x = muon::pack_bf16x2(v[0], v[1]);
-  w.y = muon::pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<uint2*>(p) = w;
+  // src: K x ld matrix (k = memory row); tile columns [col0, col0 + R).
+  __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int cols, int K, int col0,
+                                       int wave, int lane) {
+    rsrc = make_rsrc(src, static_cast<uint32_t>(static_cast<int64_t>(K) * ld * 2));
+#pragma unroll
+    for (int q = 0; q < NG; ++q) {
+      const int k = RPI * (wave + 4 * q) + lane / CPR;
+      const int c = (lane % CPR) ^ ((k & 3) << 2);
+      const int col = col0 + 8 * c;
+      kr[q] = k;
+      base[q] = (col < cols) ? static_cast<uint32_t>((static_cast<int64_t>(k) * ld + col) * 2)
+                             : kOOB;
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds, int k0, int K, int64_t ld, int wave,
+                                        bool full) const {
+    const uint32_t soff = static_cast<uint32_t>(static_cast<int64_t>(k0) * ld * 2);
+#pragma unroll
+    for (int q = 0; q < NG; ++q)
+      dma16(rsrc, lds + (wave + 4 * q) * 1024, (full || k0 + kr[q] < K) ? base[q] : kOOB, soff);
+  }
+  __device__ __forceinline__ bf16x8_t frag(const char* t, int rb, int kk, int lane) const {
+    const int gq = lane >> 4, j = lane & 15;
+    const int col = rb + 16 * (gq & 1) + 4 * (j & 3);
+    const int k = 16 * kk + 8 * (gq >> 1) + (j >> 2);
+    const i16x4_t lo = ld_tr16(t + kt_off<R>(k, col));
+    const i16x4_t hi = ld_tr16(t + kt_off<R>(k + 4, col));
+    const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+  }
+};
+
+// ---- staged output tile: BM x BN bf16 in LDS, 2 BN-byte rows; chunk swizzle
+// g(row) = 4 (row & 3) | (row >> 2) & 3 keeps both the per-lane 8-byte
+// writes (32 consecutive rows) and the transposed mirror reads on spread banks.
+template <int BN>
+__device__ __forceinline__ int ct_off(int row, int col) {
+  const int g = ((row & 3) << 2) | ((row >> 2) & 3);
+  return row * (2 * BN) + (((col >> 3) ^ g) << 4) + ((col & 7) << 1);
 }
 
 template <int... I, typename F>
@@ -124,62 +189,20 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Finish four consecutive outputs C[i][j0 .. j0 + 3] held by one lane.
-template <int EPI>
-__device__ __forceinline__ void epilogue_group(const NsGemmArgs& a, float v[4], int i, int j0,
-                                               float s, bool zero_unit, bool diag,
-                                               const bf16_t* ep, bf16_t* dst, bf16_t* dstt) {
-  if (EPI == EPI_GRAM) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = s * v[q];
-  } else if (EPI == EPI_SYMSQ) {
-    float e[4];
-    load4_bf16(ep + static_cast<int64_t>(i) * a.lde + j0, e);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) v[q] = a.cb * e[q] + a.cc * v[q];
-  } else {
-    if (zero_unit) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = 0.0f;
-    } else {
-      float e[4];
-      load4_bf16(ep + static_cast<int64_t>(i) * a.lde + j0, e);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) v[q] = s * (a.ca * e[q] + v[q]);
-    }
-  }
-  if (EPI == EPI_UPDATE) {
-    if (dst) store4_bf16(dst + static_cast<int64_t>(i) * a.ldd + j0, v);
-    if (dstt) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dstt[static_cast<int64_t>(j0 + q) * a.ldt + i] = muon::f32_to_bf16(v[q]);
-    }
-  } else if (!diag) {
-    store4_bf16(dst + static_cast<int64_t>(i) * a.ldd + j0, v);
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      dst[static_cast<int64_t>(j0 + q) * a.ldd + i] = muon::f32_to_bf16(v[q]);
-  } else {
-    // diagonal tile: keep the i <= j half and mirror it, so the stored
-    // matrix is exactly symmetric
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int j = j0 + q;
-      if (i <= j) {
-        const bf16_t h = muon::f32_to_bf16(v[q]);
-        dst[static_cast<int64_t>(i) * a.ldd + j] = h;
-        dst[static_cast<int64_t>(j) * a.ldd + i] = h;
-      }
-    }
-  }
+__device__ __forceinline__ void load4_bf16(const bf16_t* p, float v[4]) {
+  const uint2 w = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(w.x << 16);
+  v[1] = __uint_as_float(w.x & 0xffff0000u);
+  v[2] = __uint_as_float(w.y << 16);
+  v[3] = __uint_as_float(w.y & 0xffff0000u);
 }
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, bool TM, bool TN, int EPI>
 __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
-  constexpr int STAGE = (BM + BN) * 128;
+  constexpr int STAGE = (BM + BN) * BK * 2;
+  static_assert(2 * STAGE >= BM * BN * 2, "output tile must fit the stage buffers");
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int tid = threadIdx.x;
@@ -209,31 +232,31 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
     for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = (f32x16_t)(0.0f);
 
   if (!zero_unit) {
-    OperandStream<BM> sm_;
-    OperandStream<BN> sn_;
-    sm_.init(uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.pm, u))), a.ldm, a.M, m0, wave, lane);
-    sn_.init(uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.pn, u))), a.ldn, a.N, n0, wave, lane);
+    Operand<BM, TM> om;
+    Operand<BN, TN> on;
+    om.init(uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.pm, u))), a.ldm, a.M, a.K, m0,
+            wave, lane);
+    on.init(uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.pn, u))), a.ldn, a.N, a.K, n0,
+            wave, lane);
     const int KT = (a.K + BK - 1) / BK;
+    const int KF = a.K / BK;  // stages lying fully inside K
 
-    sm_.issue(smem, 0, a.K, wave, lane);
-    sn_.issue(smem + BM * 128, 0, a.K, wave, lane);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-
-    auto compute = [&](const char* sm) {
-      const char* sn = sm + BM * 128;
+    auto issue = [&](int kt) {
+      char* st = smem + (kt & 1) * STAGE;
+      const bool full = kt < KF;
+      om.issue(st, kt * BK, a.K, a.ldm, wave, full);
+      on.issue(st + BM * BK * 2, kt * BK, a.K, a.ldn, wave, full);
+    };
+    auto compute = [&](int kt) {
+      const char* sm = smem + (kt & 1) * STAGE;
+      const char* sn = sm + BM * BK * 2;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        const int chunk = 2 * kk + (lane >> 5);
         bf16x8_t fa[FN], fb[FM];
 #pragma unroll
-        for (int ni = 0; ni < FN; ++ni)
-          fa[ni] = *reinterpret_cast<const bf16x8_t*>(
-              sn + lds_off(wn * WN + ni * 32 + (lane & 31), chunk));
+        for (int ni = 0; ni < FN; ++ni) fa[ni] = on.frag(sn, wn * WN + ni * 32, kk, lane);
 #pragma unroll
-        for (int mi = 0; mi < FM; ++mi)
-          fb[mi] = *reinterpret_cast<const bf16x8_t*>(
-              sm + lds_off(wm * WM + mi * 32 + (lane & 31), chunk));
+        for (int mi = 0; mi < FM; ++mi) fb[mi] = om.frag(sm, wm * WM + mi * 32, kk, lane);
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
@@ -242,175 +265,145 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ni], fb[mi], acc[mi][ni], 0, 0, 0);
       }
     };
+
+    issue(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
     // steady state without branches: stage kt + 1 loads while stage kt computes
     for (int kt = 0; kt < KT - 1; ++kt) {
-      char* nm = smem + ((kt + 1) & 1) * STAGE;
-      sm_.issue(nm, (kt + 1) * BK, a.K, wave, lane);
-      sn_.issue(nm + BM * 128, (kt + 1) * BK, a.K, wave, lane);
-      compute(smem + (kt & 1) * STAGE);
+      issue(kt + 1);
+      compute(kt);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    compute(smem + ((KT - 1) & 1) * STAGE);
+    compute(KT - 1);
   }
 
-  // Epilogue.  MFMA operand A carried the N side, so lane l holds row
-  // i = m0 + ... + l % 32 of C and, per register group g, the four
-  // consecutive columns j0 .. j0 + 3.
+  // ---- epilogue: finish values in registers, stage bf16 tile in LDS, store.
+  // MFMA operand A carried the N side, so lane l holds local row
+  // wm WM + mi 32 + l % 32 of C and, per register group g, four consecutive
+  // local columns wn WN + ni 32 + 8 g + 4 (l / 32) + 0..3.
   float s = 1.0f;
   if (a.scale != nullptr && a.scale_pow > 0) {
     s = a.scale[u];
     if (a.scale_pow == 2) s = s * s;
   }
-  bf16_t* dst = a.dst.base || a.dst.table ? uniform_ptr(reinterpret_cast<bf16_t*>(mat_at(a.dst, u))) : nullptr;
-  bf16_t* dstt = a.dst_t.base || a.dst_t.table ? uniform_ptr(reinterpret_cast<bf16_t*>(mat_at(a.dst_t, u))) : nullptr;
-  const bf16_t* ep = (EPI == EPI_GRAM) ? nullptr : uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.epi, u)));
-  const bool diag = (EPI != EPI_UPDATE) && ti == tj;
+  const bf16_t* ep = (EPI == EPI_GRAM) ? nullptr
+                                       : uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.epi, u)));
+  __syncthreads();  // every wave is done reading the operand stages
+  char* ct = smem;
   static_for<FM>([&](auto MI) {
     constexpr int mi = decltype(MI)::value;
-    const int i = m0 + wm * WM + mi * 32 + (lane & 31);
+    const int il = wm * WM + mi * 32 + (lane & 31);
+    const int i = m0 + il;
     static_for<FN>([&](auto NI) {
       constexpr int ni = decltype(NI)::value;
       static_for<4>([&](auto G) {
         constexpr int g = decltype(G)::value;
-        const int j0 = n0 + wn * WN + ni * 32 + 8 * g + 4 * (lane >> 5);
+        const int jl = wn * WN + ni * 32 + 8 * g + 4 * (lane >> 5);
+        const int j0 = n0 + jl;
         float v[4] = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
                       acc[mi][ni][4 * g + 3]};
-        if (i < a.M && j0 < a.N)
-          epilogue_group<EPI>(a, v, i, j0, s, zero_unit, diag, ep, dst, dstt);
+        if (EPI == EPI_GRAM) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = s * v[q];
+        } else if (i < a.M && j0 < a.N) {
+          if (EPI == EPI_UPDATE && zero_unit) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = 0.0f;
+          } else {
+            float e[4];
+            load4_bf16(ep + static_cast<int64_t>(i) * a.lde + j0, e);
+            if (EPI == EPI_SYMSQ) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = a.cb * e[q] + a.cc * v[q];
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = s * (a.ca * e[q] + v[q]);
+            }
+          }
+        }
+        uint2 w;
+        w.x = muon::pack_bf16x2(v[0], v[1]);
+        w.y = muon::pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint2*>(ct + ct_off<BN>(il, jl)) = w;
       });
     });
   });
+  __syncthreads();
+
+  bf16_t* dst = uniform_ptr(reinterpret_cast<bf16_t*>(mat_at(a.dst, u)));
+  const bool diag = (EPI != EPI_UPDATE) && ti == tj;
+  constexpr int CH = BN / 8;  // 16-byte chunks per tile row
+  // primary: C rows, 16-byte row-contiguous stores (a diagonal tile of a
+  // symmetric output takes its lower half from the mirrored upper half)
+#pragma unroll 4
+  for (int e = tid; e < BM * CH; e += 256) {
+    const int rl = e / CH, c = e % CH;
+    const int i = m0 + rl, j = n0 + 8 * c;
+    if (i >= a.M || j >= a.N) continue;
+    uint4 val;
+    if (!diag || 8 * c >= rl) {
+      val = *reinterpret_cast<const uint4*>(ct + ct_off<BN>(rl, 8 * c));
+    } else {
+      uint16_t h[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int cl = 8 * c + q;
+        h[q] = (cl >= rl) ? *reinterpret_cast<const uint16_t*>(ct + ct_off<BN>(rl, cl))
+                          : *reinterpret_cast<const uint16_t*>(ct + ct_off<BN>(cl, rl));
+      }
+      val = __builtin_bit_cast(uint4, h);
+    }
+    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(i) * a.ldd + j) = val;
+  }
+  if (EPI != EPI_UPDATE && !diag) {
+    // mirror: row j of the output gets C[i .. i + 7][j] from two transposed
+    // reads; blocks of 32 columns x 16 rows, one per wave at a time
+    constexpr int BJ = BN / 32, BI = BM / 16;
+    const int gq = lane >> 4, jx = lane & 15;
+    for (int b = wave; b < BJ * BI; b += 4) {
+      const int jb = (b % BJ) * 32, ib = (b / BJ) * 16;
+      const int col = jb + 16 * (gq & 1) + 4 * (jx & 3);
+      const int row = ib + 8 * (gq >> 1) + (jx >> 2);
+      const i16x4_t lo = ld_tr16(ct + ct_off<BN>(row, col));
+      const i16x4_t hi = ld_tr16(ct + ct_off<BN>(row + 4, col));
+      const int jl = jb + 16 * (gq & 1) + jx;  // column of C = output row
+      const int il = ib + 8 * (gq >> 1);       // first of 8 rows of C = output column
+      const int orow = n0 + jl, ocol = m0 + il;
+      if (orow < a.N && ocol < a.M) {
+        const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(orow) * a.ldd + ocol) =
+            __builtin_bit_cast(uint4, v);
+      }
+    }
+  }
 }
 
-template <int T, int EPI>
+template <int T, bool TM, bool TN, int EPI>
 hipError_t go(hipStream_t s, const NsGemmArgs& a) {
   const int64_t grid = a.units * a.tiles_per_unit;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL / 256) return hipErrorInvalidValue;
-  ns_gemm_mfma_kernel<T, T, EPI><<<static_cast<unsigned>(grid), 256, 0, s>>>(a);
+  ns_gemm_mfma_kernel<T, T, TM, TN, EPI><<<static_cast<unsigned>(grid), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <int T>
-hipError_t dispatch(hipStream_t s, const NsGemmArgs& a, int epi) {
-  if (epi == EPI_GRAM) return go<T, EPI_GRAM>(s, a);
-  if (epi == EPI_SYMSQ) return go<T, EPI_SYMSQ>(s, a);
-  if (epi == EPI_UPDATE) return go<T, EPI_UPDATE>(s, a);
+hipError_t dispatch(hipStream_t s, const NsGemmArgs& a, int epi, bool tm, bool tn) {
+  if (epi == EPI_GRAM && !tm && !tn) return go<T, false, false, EPI_GRAM>(s, a);
+  if (epi == EPI_GRAM && tm && tn) return go<T, true, true, EPI_GRAM>(s, a);
+  if (epi == EPI_SYMSQ && !tm && !tn) return go<T, false, false, EPI_SYMSQ>(s, a);
+  if (epi == EPI_UPDATE && !tm && tn) return go<T, false, true, EPI_UPDATE>(s, a);
+  if (epi == EPI_UPDATE && !tm && !tn) return go<T, false, false, EPI_UPDATE>(s, a);
   return hipErrorInvalidValue;
-}
-
-// ---------------------------------------------------------------------------
-// Prep: transpose Y into the missing layout and reduce its Frobenius norm.
-// One 64 x 64 tile per workgroup; squares summed exactly in fp64 per tile,
-// then per unit in a fixed order (deterministic).
-// ---------------------------------------------------------------------------
-constexpr int PT = 64;
-
-__global__ __launch_bounds__(256) void prep_kernel(MatRef in, MatRef outT, int rows, int cols,
-                                                   int tiles_r, int tiles_c, double* partial) {
-  __shared__ uint16_t tile[PT][PT + 8];
-  __shared__ double red[256];
-  const int64_t u = blockIdx.y;
-  const int t = blockIdx.x;
-  const int tr = t % tiles_r, tc = t / tiles_r;
-  const int r0 = tr * PT, c0 = tc * PT;
-  const bf16_t* src = reinterpret_cast<const bf16_t*>(mat_at(in, u));
-  bf16_t* dst = reinterpret_cast<bf16_t*>(mat_at(outT, u));
-  const int tid = threadIdx.x;
-  double acc = 0.0;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = tid + 256 * q;  // 512 chunks of 8 elements: 64 rows x 8 chunks
-    const int r = e >> 3, c = (e & 7) * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (r0 + r < rows && c0 + c < cols)
-      v = *reinterpret_cast<const uint4*>(src + static_cast<int64_t>(r0 + r) * cols + c0 + c);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float lo = __uint_as_float(w[k] << 16), hi = __uint_as_float(w[k] & 0xffff0000u);
-      acc += static_cast<double>(lo * lo);
-      acc += static_cast<double>(hi * hi);
-      tile[r][c + 2 * k] = static_cast<uint16_t>(w[k] & 0xffffu);
-      tile[r][c + 2 * k + 1] = static_cast<uint16_t>(w[k] >> 16);
-    }
-  }
-  red[tid] = acc;
-  __syncthreads();
-  // transposed write: out row (c0 + c) holds column c of the tile
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int e = tid + 256 * q;
-    const int c = e >> 3, r = (e & 7) * 8;
-    if (c0 + c < cols && r0 + r < rows) {
-      uint4 o;
-      o.x = tile[r + 0][c] | (static_cast<uint32_t>(tile[r + 1][c]) << 16);
-      o.y = tile[r + 2][c] | (static_cast<uint32_t>(tile[r + 3][c]) << 16);
-      o.z = tile[r + 4][c] | (static_cast<uint32_t>(tile[r + 5][c]) << 16);
-      o.w = tile[r + 6][c] | (static_cast<uint32_t>(tile[r + 7][c]) << 16);
-      *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(c0 + c) * rows + r0 + r) = o;
-    }
-  }
-#pragma unroll
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) partial[u * (static_cast<int64_t>(tiles_r) * tiles_c) + t] = red[0];
-}
-
-__global__ __launch_bounds__(256) void prep_finalize_kernel(const double* partial, int parts,
-                                                            float* scale, int* zflag,
-                                                            int* nonfinite, float eps) {
-  __shared__ double red[256];
-  const int64_t u = blockIdx.x;
-  const int tid = threadIdx.x;
-  double acc = 0.0;
-  for (int p = tid; p < parts; p += 256) acc += partial[u * parts + p];
-  red[tid] = acc;
-  __syncthreads();
-#pragma unroll
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] += red[tid + w];
-    __syncthreads();
-  }
-  if (tid == 0) {
-    const double sq = red[0];
-    scale[u] = static_cast<float>(1.0 / (sqrt(sq) + static_cast<double>(eps)));
-    zflag[u] = (sq == 0.0) ? 1 : 0;
-    if (nonfinite && !isfinite(sq)) atomicOr(nonfinite, 1);
-  }
 }
 
 }  // namespace
 
-hipError_t launch_ns_gemm_mfma(hipStream_t s, const NsGemmArgs& a, int epi, int tile) {
-  if (tile == 256) return dispatch<256>(s, a, epi);
-  if (tile == 128) return dispatch<128>(s, a, epi);
+hipError_t launch_ns_gemm_mfma(hipStream_t s, const NsGemmArgs& a, int epi, bool trans_m,
+                               bool trans_n, int tile) {
+  if (tile == 256) return dispatch<256>(s, a, epi, trans_m, trans_n);
+  if (tile == 128) return dispatch<128>(s, a, epi, trans_m, trans_n);
   return hipErrorInvalidValue;
-}
-
-int prep_parts(int rows, int cols) { return ((rows + PT - 1) / PT) * ((cols + PT - 1) / PT); }
-
-hipError_t launch_prep(hipStream_t s, MatRef in, MatRef outT, int rows, int cols, int64_t units,
-                       double* partial, float* scale, int* zflag, int* nonfinite, float eps) {
-  const int tr = (rows + PT - 1) / PT, tc = (cols + PT - 1) / PT;
-  constexpr int64_t kMaxY = 65535;
-  for (int64_t u0 = 0; u0 < units; u0 += kMaxY) {
-    const int64_t n = (units - u0 < kMaxY) ? units - u0 : kMaxY;
-    MatRef i0 = in, o0 = outT;
-    if (i0.table) i0.table += u0; else i0.base += u0 * i0.stride;
-    if (o0.table) o0.table += u0; else o0.base += u0 * o0.stride;
-    double* p0 = partial + u0 * static_cast<int64_t>(tr) * tc;
-    prep_kernel<<<dim3(static_cast<unsigned>(tr * tc), static_cast<unsigned>(n)), 256, 0, s>>>(
-        i0, o0, rows, cols, tr, tc, p0);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    prep_finalize_kernel<<<static_cast<unsigned>(n), 256, 0, s>>>(p0, tr * tc, scale + u0,
-                                                                   zflag + u0, nonfinite, eps);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
 }

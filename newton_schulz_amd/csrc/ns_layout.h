@@ -7,7 +7,7 @@
 
 // Per call: `units` Newton-Schulz units of ur x uc (m = min, n = max).
 // Regions (byte offsets into the workspace, 256-byte aligned):
-//   xa..xd   four m*n iterate buffers: the iterate X and X^T, ping-pong
+//   xa, xb   two m*n iterate buffers        (ping-pong)
 //   a, b     two m*m buffers                (A = X X^T, B = bA + cA^2)
 //   scale    float per unit                 1 / (||Y||_F + eps)
 //   zflag    int per unit                   ||Y||_F == 0
@@ -16,9 +16,7 @@ struct NsLayout {
   int64_t units = 0, ur = 0, uc = 0, m = 0, n = 0;
   int parts = 1;
   int64_t chunk = 0;
-  size_t xa = 0, xb = 0, xc = 0, xd = 0, a = 0, b = 0, scale = 0, zflag = 0, partial = 0,
-         total = 0;
-  int partial_slots = 1;  // per unit: max of the norm and the prep partial counts
+  size_t xa = 0, xb = 0, a = 0, b = 0, scale = 0, zflag = 0, partial = 0, total = 0;
 };
 
 bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* L);

@@ -45,21 +45,17 @@ bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* 
   parts = (ue + chunk - 1) / chunk;
   l.parts = static_cast<int>(parts);
   l.chunk = chunk;
-  const int64_t prep = ((l.ur + 63) / 64) * ((l.uc + 63) / 64);  // 64 x 64 prep tiles
-  l.partial_slots = static_cast<int>(std::max<int64_t>(parts, prep));
   const size_t U = static_cast<size_t>(l.units);
   const size_t xbytes = align_up(U * static_cast<size_t>(l.m * l.n) * e);
   const size_t abytes = align_up(U * static_cast<size_t>(l.m * l.m) * e);
   size_t off = 0;
   l.xa = off; off += xbytes;
   l.xb = off; off += xbytes;
-  l.xc = off; off += xbytes;
-  l.xd = off; off += xbytes;
   l.a = off; off += abytes;
   l.b = off; off += abytes;
   l.scale = off; off += align_up(U * 4);
   l.zflag = off; off += align_up(U * 4);
-  l.partial = off; off += align_up(U * static_cast<size_t>(l.partial_slots) * 8);
+  l.partial = off; off += align_up(U * static_cast<size_t>(l.parts) * 8);
   l.total = count == 0 ? 0 : off;
   *L = l;
   return true;
