@@ -178,6 +178,17 @@ __device__ __forceinline__ int ct_off(int row, int col) {
   return row * (2 * BN) + (((col >> 3) ^ g) << 4) + ((col & 7) << 1);
 }
 
+// The staged tile spans both stage buffers: rows [0, BM / 2) in the first,
+// the rest in the second.
+template <int BM, int BN>
+struct OutTile {
+  char* lo;
+  char* hi;
+  __device__ __forceinline__ char* at(int row, int col) const {
+    return row < BM / 2 ? lo + ct_off<BN>(row, col) : hi + ct_off<BN>(row - BM / 2, col);
+  }
+};
+
 template <int... I, typename F>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);
@@ -203,7 +214,11 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int STAGE = (BM + BN) * BK * 2;
   static_assert(2 * STAGE >= BM * BN * 2, "output tile must fit the stage buffers");
-  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
+  // Two distinct LDS objects for the two stages: the DMA writes into one are
+  // then provably disjoint from the reads of the other, so no wait on the
+  // loads in flight is inserted ahead of the MFMA loop.
+  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -241,14 +256,14 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
     const int KT = (a.K + BK - 1) / BK;
     const int KF = a.K / BK;  // stages lying fully inside K
 
-    auto issue = [&](int kt) {
-      char* st = smem + (kt & 1) * STAGE;
+    auto issue = [&](char* st, int kt) {
       const bool full = kt < KF;
       om.issue(st, kt * BK, a.K, a.ldm, wave, full);
       on.issue(st + BM * BK * 2, kt * BK, a.K, a.ldn, wave, full);
+      // keep the loads ahead of the MFMAs they are meant to overlap
+      __builtin_amdgcn_sched_barrier(0);
     };
-    auto compute = [&](int kt) {
-      const char* sm = smem + (kt & 1) * STAGE;
+    auto compute = [&](const char* sm) {
       const char* sn = sm + BM * BK * 2;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
@@ -265,18 +280,26 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ni], fb[mi], acc[mi][ni], 0, 0, 0);
       }
     };
-
-    issue(0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    // steady state without branches: stage kt + 1 loads while stage kt computes
-    for (int kt = 0; kt < KT - 1; ++kt) {
-      issue(kt + 1);
-      compute(kt);
+    auto sync = [&]() {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+    };
+
+    // Stage kt + 1 loads while stage kt computes; even stages in stage0, odd
+    // in stage1 (unrolled by two so each buffer is a fixed object).  The loop
+    // always runs whole pairs: a stage at or past K loads zeros (its offsets
+    // fall outside the buffer), so an odd stage count costs one zero stage
+    // and the body has no branches.
+    issue(stage0, 0);
+    sync();
+    for (int kt = 0; kt < KT; kt += 2) {
+      issue(stage1, kt + 1);
+      compute(stage0);
+      sync();
+      issue(stage0, kt + 2);
+      compute(stage1);
+      sync();
     }
-    compute(KT - 1);
   }
 
   // ---- epilogue: finish values in registers, stage bf16 tile in LDS, store.
@@ -291,7 +314,8 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
   const bf16_t* ep = (EPI == EPI_GRAM) ? nullptr
                                        : uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.epi, u)));
   __syncthreads();  // every wave is done reading the operand stages
-  char* ct = smem;
+  static_assert(STAGE >= (BM / 2) * BN * 2, "half of the output tile per stage buffer");
+  const OutTile<BM, BN> ct{stage0, stage1};
   static_for<FM>([&](auto MI) {
     constexpr int mi = decltype(MI)::value;
     const int il = wm * WM + mi * 32 + (lane & 31);
@@ -326,8 +350,11 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
         uint2 w;
         w.x = muon::pack_bf16x2(v[0], v[1]);
         w.y = muon::pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(ct + ct_off<BN>(il, jl)) = w;
+        *reinterpret_cast<uint2*>(ct.at(il, jl)) = w;
       });
+      // one 32 x 32 block at a time: keeps accumulator reads from being
+      // hoisted all together (register pressure)
+      __builtin_amdgcn_sched_barrier(0);
     });
   });
   __syncthreads();
@@ -344,14 +371,14 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
     if (i >= a.M || j >= a.N) continue;
     uint4 val;
     if (!diag || 8 * c >= rl) {
-      val = *reinterpret_cast<const uint4*>(ct + ct_off<BN>(rl, 8 * c));
+      val = *reinterpret_cast<const uint4*>(ct.at(rl, 8 * c));
     } else {
       uint16_t h[8];
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int cl = 8 * c + q;
-        h[q] = (cl >= rl) ? *reinterpret_cast<const uint16_t*>(ct + ct_off<BN>(rl, cl))
-                          : *reinterpret_cast<const uint16_t*>(ct + ct_off<BN>(cl, rl));
+        h[q] = (cl >= rl) ? *reinterpret_cast<const uint16_t*>(ct.at(rl, cl))
+                          : *reinterpret_cast<const uint16_t*>(ct.at(cl, rl));
       }
       val = __builtin_bit_cast(uint4, h);
     }
@@ -366,8 +393,8 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
       const int jb = (b % BJ) * 32, ib = (b / BJ) * 16;
       const int col = jb + 16 * (gq & 1) + 4 * (jx & 3);
       const int row = ib + 8 * (gq >> 1) + (jx >> 2);
-      const i16x4_t lo = ld_tr16(ct + ct_off<BN>(row, col));
-      const i16x4_t hi = ld_tr16(ct + ct_off<BN>(row + 4, col));
+      const i16x4_t lo = ld_tr16(ct.at(row, col));
+      const i16x4_t hi = ld_tr16(ct.at(row + 4, col));
       const int jl = jb + 16 * (gq & 1) + jx;  // column of C = output row
       const int il = ib + 8 * (gq >> 1);       // first of 8 rows of C = output column
       const int orow = n0 + jl, ocol = m0 + il;
