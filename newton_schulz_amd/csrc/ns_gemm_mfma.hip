@@ -200,14 +200,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-__device__ __forceinline__ void load4_bf16(const bf16_t* p, float v[4]) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(w.x << 16);
-  v[1] = __uint_as_float(w.x & 0xffff0000u);
-  v[2] = __uint_as_float(w.y << 16);
-  v[3] = __uint_as_float(w.y & 0xffff0000u);
-}
-
 template <int BM, int BN, bool TM, bool TN, int EPI>
 __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
   constexpr int WM = BM / 2, WN = BN / 2;
@@ -311,46 +303,71 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
     s = a.scale[u];
     if (a.scale_pow == 2) s = s * s;
   }
-  const bf16_t* ep = (EPI == EPI_GRAM) ? nullptr
-                                       : uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.epi, u)));
   __syncthreads();  // every wave is done reading the operand stages
   static_assert(STAGE >= (BM / 2) * BN * 2, "half of the output tile per stage buffer");
   const OutTile<BM, BN> ct{stage0, stage1};
+  // symsq and update add a multiple of an input tile (A, or X / Y): fetch
+  // that tile into the staging area with one round of global->LDS loads,
+  // laid out exactly like the output tile, and finish the values in place.
+  const bool need_src = (EPI != EPI_GRAM) && !zero_unit;
+  if (need_src) {
+    const bf16_t* ep = uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.epi, u)));
+    const __amdgpu_buffer_rsrc_t er =
+        make_rsrc(ep, static_cast<uint32_t>(static_cast<int64_t>(a.M) * a.lde * 2));
+    constexpr int RB = 2 * BN;                 // bytes per staged row
+    constexpr int HALF = (BM / 2) * RB / 1024; // wave instructions per half tile
+#pragma unroll
+    for (int q = 0; q < 2 * HALF / 4; ++q) {
+      const int g = wave + 4 * q;
+      const int h = g >= HALF;                 // which stage buffer
+      const int pos = (g - h * HALF) * 1024 + lane * 16;
+      const int rl = pos / RB;                 // row within the half
+      const int pc = (pos % RB) >> 4;          // physical chunk
+      const int gsw = ((rl & 3) << 2) | ((rl >> 2) & 3);
+      const int row = rl + h * (BM / 2);
+      const int col = 8 * (pc ^ gsw);
+      const int gi = m0 + row, gj = n0 + col;
+      const uint32_t off = (gi < a.M && gj < a.N)
+                               ? static_cast<uint32_t>((static_cast<int64_t>(gi) * a.lde + gj) * 2)
+                               : kOOB;
+      dma16(er, (h ? stage1 : stage0) + (g - h * HALF) * 1024, off, 0);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
   static_for<FM>([&](auto MI) {
     constexpr int mi = decltype(MI)::value;
     const int il = wm * WM + mi * 32 + (lane & 31);
-    const int i = m0 + il;
     static_for<FN>([&](auto NI) {
       constexpr int ni = decltype(NI)::value;
       static_for<4>([&](auto G) {
         constexpr int g = decltype(G)::value;
         const int jl = wn * WN + ni * 32 + 8 * g + 4 * (lane >> 5);
-        const int j0 = n0 + jl;
         float v[4] = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
                       acc[mi][ni][4 * g + 3]};
+        uint2* slot = reinterpret_cast<uint2*>(ct.at(il, jl));
         if (EPI == EPI_GRAM) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = s * v[q];
-        } else if (i < a.M && j0 < a.N) {
-          if (EPI == EPI_UPDATE && zero_unit) {
+        } else if (!need_src) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = 0.0f;
+          for (int q = 0; q < 4; ++q) v[q] = 0.0f;
+        } else {
+          const uint2 w = *slot;
+          const float e[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                              __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+          if (EPI == EPI_SYMSQ) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = a.cb * e[q] + a.cc * v[q];
           } else {
-            float e[4];
-            load4_bf16(ep + static_cast<int64_t>(i) * a.lde + j0, e);
-            if (EPI == EPI_SYMSQ) {
 #pragma unroll
-              for (int q = 0; q < 4; ++q) v[q] = a.cb * e[q] + a.cc * v[q];
-            } else {
-#pragma unroll
-              for (int q = 0; q < 4; ++q) v[q] = s * (a.ca * e[q] + v[q]);
-            }
+            for (int q = 0; q < 4; ++q) v[q] = s * (a.ca * e[q] + v[q]);
           }
         }
         uint2 w;
         w.x = muon::pack_bf16x2(v[0], v[1]);
         w.y = muon::pack_bf16x2(v[2], v[3]);
-        *reinterpret_cast<uint2*>(ct.at(il, jl)) = w;
+        *slot = w;
       });
       // one 32 x 32 block at a time: keeps accumulator reads from being
       // hoisted all together (register pressure)
