@@ -66,14 +66,14 @@ def unit_list(w):
 def traffic_record(kernel_src: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     counter summary, or None when missing or taken on a different source."""
-    path = os.path.join(ROOT, "profiles", "update_kernel_traffic.json")
+    path = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_4b.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
     if rec.get("source_sha256_16") != h:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return round(rec.get("hbm_bytes_per_launch"))
 
 
 def cpu_baseline(seconds_budget: float = 20.0):
@@ -142,6 +142,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_4b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip per-kernel event timing")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus})",
@@ -153,6 +155,14 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}), flush=True)
+        return
     w = workload_by_name(args.workload)
     shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
     keep_bf16 = args.workload != "qwen3_30b_experts"

@@ -222,8 +222,15 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
   const int t = static_cast<int>(lid - u * a.tiles_per_unit);
   int ti, tj;
   if (EPI == EPI_UPDATE) {
-    ti = t % a.tiles_m;
-    tj = t / a.tiles_m;
+    // grouped raster: bands of up to GN tile columns, row-major inside a
+    // band, so the ~32 tiles an XCD runs at once form an 8 x 4 block that
+    // shares its operand panels in L2
+    constexpr int GN = 4;
+    const int band = t / (a.tiles_m * GN);
+    const int w = min(GN, a.tiles_n - band * GN);
+    const int r = t - band * a.tiles_m * GN;
+    ti = r / w;
+    tj = band * GN + r % w;
   } else {
     upper_tile(t, ti, tj);
   }
