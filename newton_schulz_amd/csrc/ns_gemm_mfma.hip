@@ -17,8 +17,12 @@
 // four consecutive k of one column, so no transposed copy of any matrix is
 // ever made.
 //
-// Tiling: BM x BN workgroup tile, BK = 64, 256 threads = 4 waves in 2 x 2,
-// each wave (BM/2) x (BN/2) as 32 x 32 MFMA tiles.  Operand tiles move
+// Tiling: BM x BN workgroup tile, BK = 64.  256 x 256 tiles run 8 waves
+// (2 along M x 4 along N, two waves per SIMD, each 128 x 64): a second wave
+// on every SIMD issues its LDS reads and MFMAs while the first waits, which a
+// single wave per SIMD cannot hide.  128 x 128 tiles run 4 waves of 64 x 64.
+// MFMA fragments are double-buffered in registers: the LDS reads of k16 step
+// kk + 1 are interleaved with the MFMAs of step kk.  Operand tiles move
 // global -> LDS with buffer_load_dwordx4 ... lds: each wave instruction
 // fills 1024 contiguous LDS bytes (lane l at 16 l), so every lane fetches the
 // global chunk the XOR swizzle puts at its slot; chunks outside the matrix get
@@ -91,12 +95,12 @@ __device__ __forceinline__ int kt_off(int k, int col) {
   return k * (2 * R) + (((col >> 3) ^ ((k & 3) << 2)) << 4) + ((col & 7) << 1);
 }
 
-template <int R, bool KMAJOR>
+template <int R, bool KMAJOR, int NW>
 struct Operand;
 
-template <int R>
-struct Operand<R, false> {
-  static constexpr int NG = R / 32;  // 8 rows per wave instruction, 4 waves
+template <int R, int NW>
+struct Operand<R, false, NW> {
+  static constexpr int NG = R / (8 * NW);  // 8 rows per wave instruction
   uint32_t base[NG];
   int kc[NG];
   __amdgpu_buffer_rsrc_t rsrc;
@@ -107,7 +111,7 @@ struct Operand<R, false> {
     rsrc = make_rsrc(src, static_cast<uint32_t>(static_cast<int64_t>(rows) * ld * 2));
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
-      const int row = 8 * (wave + 4 * q) + (lane >> 3);
+      const int row = 8 * (wave + NW * q) + (lane >> 3);
       const int lc = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
       const int gr = row0 + row;
       kc[q] = 8 * lc;
@@ -120,7 +124,7 @@ struct Operand<R, false> {
     const uint32_t soff = static_cast<uint32_t>(k0 * 2);
 #pragma unroll
     for (int q = 0; q < NG; ++q)
-      dma16(rsrc, lds + (wave + 4 * q) * 1024, (full || k0 + kc[q] < K) ? base[q] : kOOB, soff);
+      dma16(rsrc, lds + (wave + NW * q) * 1024, (full || k0 + kc[q] < K) ? base[q] : kOOB, soff);
   }
   // MFMA operand for tile rows rb .. rb + 31, k = 16 kk + 8 (lane / 32) + 0..7
   __device__ __forceinline__ bf16x8_t frag(const char* t, int rb, int kk, int lane) const {
@@ -128,11 +132,11 @@ struct Operand<R, false> {
   }
 };
 
-template <int R>
-struct Operand<R, true> {
+template <int R, int NW>
+struct Operand<R, true, NW> {
   static constexpr int CPR = R / 8;         // 16-byte chunks per tile row
   static constexpr int RPI = 64 / CPR;      // tile rows per wave instruction
-  static constexpr int NG = BK / RPI / 4;   // instructions per wave
+  static constexpr int NG = BK / RPI / NW;  // instructions per wave
   uint32_t base[NG];
   int kr[NG];
   __amdgpu_buffer_rsrc_t rsrc;
@@ -143,7 +147,7 @@ struct Operand<R, true> {
     rsrc = make_rsrc(src, static_cast<uint32_t>(static_cast<int64_t>(K) * ld * 2));
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
-      const int k = RPI * (wave + 4 * q) + lane / CPR;
+      const int k = RPI * (wave + NW * q) + lane / CPR;
       const int c = (lane % CPR) ^ ((k & 3) << 2);
       const int col = col0 + 8 * c;
       kr[q] = k;
@@ -156,7 +160,7 @@ struct Operand<R, true> {
     const uint32_t soff = static_cast<uint32_t>(static_cast<int64_t>(k0) * ld * 2);
 #pragma unroll
     for (int q = 0; q < NG; ++q)
-      dma16(rsrc, lds + (wave + 4 * q) * 1024, (full || k0 + kr[q] < K) ? base[q] : kOOB, soff);
+      dma16(rsrc, lds + (wave + NW * q) * 1024, (full || k0 + kr[q] < K) ? base[q] : kOOB, soff);
   }
   __device__ __forceinline__ bf16x8_t frag(const char* t, int rb, int kk, int lane) const {
     const int gq = lane >> 4, j = lane & 15;
@@ -200,9 +204,10 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <int BM, int BN, bool TM, bool TN, int EPI>
-__global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
-  constexpr int WM = BM / 2, WN = BN / 2;
+template <int BM, int BN, int NWN, bool TM, bool TN, int EPI>
+__global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
+  constexpr int NW = 2 * NWN, NT = 64 * NW;  // waves: 2 along M x NWN along N
+  constexpr int WM = BM / 2, WN = BN / NWN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int STAGE = (BM + BN) * BK * 2;
   static_assert(2 * STAGE >= BM * BN * 2, "output tile must fit the stage buffers");
@@ -215,7 +220,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / NWN, wn = wave % NWN;
 
   const int64_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
   const int64_t u = lid / a.tiles_per_unit;
@@ -246,58 +251,96 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
     for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = (f32x16_t)(0.0f);
 
   if (!zero_unit) {
-    Operand<BM, TM> om;
-    Operand<BN, TN> on;
+    Operand<BM, TM, NW> om;
+    Operand<BN, TN, NW> on;
     om.init(uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.pm, u))), a.ldm, a.M, a.K, m0,
             wave, lane);
     on.init(uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.pn, u))), a.ldn, a.N, a.K, n0,
             wave, lane);
     const int KT = (a.K + BK - 1) / BK;
     const int KF = a.K / BK;  // stages lying fully inside K
-
     auto issue = [&](char* st, int kt) {
       const bool full = kt < KF;
       om.issue(st, kt * BK, a.K, a.ldm, wave, full);
       on.issue(st + BM * BK * 2, kt * BK, a.K, a.ldn, wave, full);
-      // keep the loads ahead of the MFMAs they are meant to overlap
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    auto compute = [&](const char* sm) {
-      const char* sn = sm + BM * BK * 2;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        bf16x8_t fa[FN], fb[FM];
-#pragma unroll
-        for (int ni = 0; ni < FN; ++ni) fa[ni] = on.frag(sn, wn * WN + ni * 32, kk, lane);
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi) fb[mi] = om.frag(sm, wm * WM + mi * 32, kk, lane);
-#pragma unroll
-        for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < FN; ++ni)
-            acc[mi][ni] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ni], fb[mi], acc[mi][ni], 0, 0, 0);
-      }
-    };
-    auto sync = [&]() {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
     };
 
-    // Stage kt + 1 loads while stage kt computes; even stages in stage0, odd
-    // in stage1 (unrolled by two so each buffer is a fixed object).  The loop
-    // always runs whole pairs: a stage at or past K loads zeros (its offsets
-    // fall outside the buffer), so an odd stage count costs one zero stage
-    // and the body has no branches.
+    // Register double buffer of MFMA fragments: the LDS reads of k16 step
+    // kk + 1 are issued among the MFMAs of step kk.
+    bf16x8_t fa[2][FN], fb[2][FM];
+    auto frags = [&](const char* sm, int kk, auto BUF) {
+      constexpr int b = decltype(BUF)::value;
+      const char* sn = sm + BM * BK * 2;
+#pragma unroll
+      for (int ni = 0; ni < FN; ++ni) fa[b][ni] = on.frag(sn, wn * WN + ni * 32, kk, lane);
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi) fb[b][mi] = om.frag(sm, wm * WM + mi * 32, kk, lane);
+    };
+    auto mfmas = [&](auto BUF, auto BEGIN, auto END) {
+      constexpr int b = decltype(BUF)::value;
+      static_for<decltype(END)::value - decltype(BEGIN)::value>([&](auto P) {
+        constexpr int p = decltype(P)::value + decltype(BEGIN)::value;
+        constexpr int mi = p / FN, ni = p % FN;
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][ni], fb[b][mi], acc[mi][ni], 0, 0, 0);
+      });
+    };
+    constexpr int NMF = FM * FN;                                     // MFMAs per k16 step
+    constexpr int NRD = (TN ? 2 : 1) * FN + (TM ? 2 : 1) * FM;       // LDS reads per k16 step
+    constexpr int TAIL = NMF / 2;                                    // MFMAs after the barrier
+    // interleave: one MFMA, then one LDS read, while reads remain
+    auto interleave = [&](auto NM) {
+      static_for<decltype(NM)::value>([&](auto I) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);            // MFMA
+        if constexpr (decltype(I)::value < NRD)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // DS read
+      });
+    };
+
+    // One stage in buffer `cur` (its k16-step-0 fragments already in fa/fb[0]);
+    // the next stage sits in `nxt`; after the barrier, the stage two ahead is
+    // loaded into `cur`.
+    auto stage = [&](const char* cur, const char* nxt, char* cur_w, int kt_next2) {
+      static_for<BK / 16>([&](auto KK) {
+        constexpr int kk = decltype(KK)::value;
+        constexpr int b = kk & 1;
+        if constexpr (kk + 1 < BK / 16) {
+          frags(cur, kk + 1, std::integral_constant<int, b ^ 1>{});
+          mfmas(std::integral_constant<int, b>{}, std::integral_constant<int, 0>{},
+                std::integral_constant<int, NMF>{});
+          interleave(std::integral_constant<int, NMF>{});
+          __builtin_amdgcn_sched_barrier(0);
+        } else {
+          mfmas(std::integral_constant<int, b>{}, std::integral_constant<int, 0>{},
+                std::integral_constant<int, NMF - TAIL>{});
+          __builtin_amdgcn_sched_barrier(0);
+          // every read of `cur` done, this wave's loads of the next stage done
+          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+          __syncthreads();
+          issue(cur_w, kt_next2);
+          __builtin_amdgcn_sched_barrier(0);
+          frags(nxt, 0, std::integral_constant<int, 0>{});
+          mfmas(std::integral_constant<int, b>{}, std::integral_constant<int, NMF - TAIL>{},
+                std::integral_constant<int, NMF>{});
+          interleave(std::integral_constant<int, TAIL>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    };
+
+    // Stage kt + 1 loads while stage kt computes; it is issued at the barrier
+    // near the end of stage kt - 1, once every wave has finished reading the
+    // buffer it overwrites.  Even stages live in stage0, odd in stage1 (two
+    // fixed LDS objects, loop unrolled by two).  The loop runs whole pairs:
+    // stages at or past K load zeros (offsets fall outside the buffer), so
+    // the body has no branches.
     issue(stage0, 0);
-    sync();
+    issue(stage1, 1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    frags(stage0, 0, std::integral_constant<int, 0>{});
     for (int kt = 0; kt < KT; kt += 2) {
-      issue(stage1, kt + 1);
-      compute(stage0);
-      sync();
-      issue(stage0, kt + 2);
-      compute(stage1);
-      sync();
+      stage(stage0, stage1, stage0, kt + 2);
+      stage(stage1, stage0, stage1, kt + 3);
     }
   }
 
@@ -310,7 +353,10 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
     s = a.scale[u];
     if (a.scale_pow == 2) s = s * s;
   }
-  __syncthreads();  // every wave is done reading the operand stages
+  // every wave is done reading the operand stages, and the (zero-filled)
+  // loads the last k-stages issued past K have landed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
   static_assert(STAGE >= (BM / 2) * BN * 2, "half of the output tile per stage buffer");
   const OutTile<BM, BN> ct{stage0, stage1};
   // symsq and update add a multiple of an input tile (A, or X / Y): fetch
@@ -324,8 +370,8 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
     constexpr int RB = 2 * BN;                 // bytes per staged row
     constexpr int HALF = (BM / 2) * RB / 1024; // wave instructions per half tile
 #pragma unroll
-    for (int q = 0; q < 2 * HALF / 4; ++q) {
-      const int g = wave + 4 * q;
+    for (int q = 0; q < 2 * HALF / NW; ++q) {
+      const int g = wave + NW * q;
       const int h = g >= HALF;                 // which stage buffer
       const int pos = (g - h * HALF) * 1024 + lane * 16;
       const int rl = pos / RB;                 // row within the half
@@ -389,7 +435,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
   // primary: C rows, 16-byte row-contiguous stores (a diagonal tile of a
   // symmetric output takes its lower half from the mirrored upper half)
 #pragma unroll 4
-  for (int e = tid; e < BM * CH; e += 256) {
+  for (int e = tid; e < BM * CH; e += NT) {
     const int rl = e / CH, c = e % CH;
     const int i = m0 + rl, j = n0 + 8 * c;
     if (i >= a.M || j >= a.N) continue;
@@ -413,7 +459,7 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
     // reads; blocks of 32 columns x 16 rows, one per wave at a time
     constexpr int BJ = BN / 32, BI = BM / 16;
     const int gq = lane >> 4, jx = lane & 15;
-    for (int b = wave; b < BJ * BI; b += 4) {
+    for (int b = wave; b < BJ * BI; b += NW) {
       const int jb = (b % BJ) * 32, ib = (b / BJ) * 16;
       const int col = jb + 16 * (gq & 1) + 4 * (jx & 3);
       const int row = ib + 8 * (gq >> 1) + (jx >> 2);
@@ -433,10 +479,12 @@ __global__ __launch_bounds__(256, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
 
 template <int T, bool TM, bool TN, int EPI>
 hipError_t go(hipStream_t s, const NsGemmArgs& a) {
+  // 256 x 256 tiles: 8 waves (two per SIMD) of 128 x 64; 128 x 128: 4 waves of 64 x 64
+  constexpr int NWN = T == 256 ? 4 : 2;
   const int64_t grid = a.units * a.tiles_per_unit;
   if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL / 256) return hipErrorInvalidValue;
-  ns_gemm_mfma_kernel<T, T, TM, TN, EPI><<<static_cast<unsigned>(grid), 256, 0, s>>>(a);
+  if (grid > 0x7fffffffLL / 512) return hipErrorInvalidValue;
+  ns_gemm_mfma_kernel<T, T, NWN, TM, TN, EPI><<<static_cast<unsigned>(grid), 128 * NWN, 0, s>>>(a);
   return hipGetLastError();
 }
 
