@@ -238,7 +238,7 @@ def main():
             traffic = traffic_record(os.path.join(ROOT, "newton_schulz_amd", "csrc", "ns_gemm_mfma.hip"))
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                        "traffic": traffic, "kernel": "ns_gemm_mfma_kernel (update X' = a X + B X)",
+                        "traffic": traffic, "kernel": "ns_gemm_mfma_kernel (update X' = B' X, B' = a I + b A + c A A)",
                         "avg_launch_ms": round(t_upd / n_upd, 4),
                         "flop_per_launch_avg": int(f_upd / n_upd)}
 

@@ -50,6 +50,8 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
  * iterations (section 2, Root Cause Analysis).  Per iteration, on the
  * normalised matrix X (m x n, m <= n):
  *     A = X X^T ;  B = b A + c A A ;  X <- a X + B X
+ * (the library forms B' = a I + B and computes X <- B' X, the same product
+ * with one operand fewer).
  * X_0 = Y / (||Y||_F + eps); a tall Y (rows > cols) is processed as Y^T and
  * the result transposed back.  Defaults (muon_ns_params_default):
  * steps 5, (a, b, c) = (3.4445, -4.7750, 2.0315), eps 1e-7, compute BF16. */

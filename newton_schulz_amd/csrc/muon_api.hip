@@ -467,19 +467,18 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
 
     NsGemmArgs ua{};
     ua.dst = dstX;
-    ua.epi = src;
     ua.scale = scale;
     ua.scale_pow = (k == 0) ? 1 : 0;
     ua.zero_write = last ? 1 : 0;
     if (!tall) {
-      // X' = a X + B X : rows from B, columns from X (K-major)
+      // X' = B' X : rows from B', columns from X (K-major)
       ua.pm = BR; ua.ldm = m;
       ua.pn = src; ua.ldn = n;
       ua.ldd = ua.lde = n;
       ua.M = static_cast<int>(m);
       ua.N = static_cast<int>(n);
     } else {
-      // Y' = a Y + Y B : rows from Y, columns from B (symmetric)
+      // Y' = Y B' : rows from Y, columns from B' (symmetric)
       ua.pm = src; ua.ldm = m;
       ua.pn = BR; ua.ldn = m;
       ua.ldd = ua.lde = m;

@@ -19,7 +19,8 @@ enum NsEpi : int {
 // (element (r, k) at k * ld + r) instead of K-contiguous (r * ld + k).  dst
 // receives C row-major.
 struct NsGemmArgs {
-  MatRef pm, pn, dst, epi;
+  MatRef pm, pn, dst;
+  MatRef epi;                  // EPI_SYMSQ: the matrix A of the b A term
   int64_t ldm, ldn, ldd, lde;  // leading dimensions in elements
   int M, N, K;
   int tiles_m, tiles_n, tiles_per_unit;

@@ -3,9 +3,11 @@
 //
 // Per iteration, with X the m x n iterate (m <= n; a tall matrix Y = X^T is
 // kept in its own orientation):
-//   gram   A  = alpha X X^T      upper-triangle tiles only, mirrored
-//   symsq  B  = b A + c A A      A symmetric, so A A = A A^T; upper tiles
-//   update X' = beta (a X + B X) (tall: Y' = beta (a Y + Y B))
+//   gram   A  = alpha X X^T          upper-triangle tiles only, mirrored
+//   symsq  B' = a I + b A + c A A    A symmetric, so A A = A A^T; upper tiles
+//   update X' = beta B' X            (tall: Y' = beta Y B')
+// B' X equals the iteration's a X + B X with B = b A + c A A; carrying the
+// a I term inside B' means the update reads no third operand.
 // alpha = s^2 and beta = s fold the first iteration's normalisation
 // X_0 = s Y (s = 1 / (||Y||_F + eps)) into the products, so Y is never
 // rewritten.  Every product is C = P_M P_N^T over a contraction index k.  An
@@ -44,6 +46,7 @@ using muon::bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr_t;
 
@@ -359,11 +362,11 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   __syncthreads();
   static_assert(STAGE >= (BM / 2) * BN * 2, "half of the output tile per stage buffer");
   const OutTile<BM, BN> ct{stage0, stage1};
-  // symsq and update add a multiple of an input tile (A, or X / Y): fetch
-  // that tile into the staging area with one round of global->LDS loads,
-  // laid out exactly like the output tile, and finish the values in place.
-  const bool need_src = (EPI != EPI_GRAM) && !zero_unit;
-  if (need_src) {
+  // symsq adds b A: fetch that tile of A into the staging area with one round
+  // of global->LDS loads, laid out exactly like the output tile, and finish
+  // the values in place.
+  const bool diag_tile = ti == tj;
+  if (EPI == EPI_SYMSQ) {
     const bf16_t* ep = uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.epi, u)));
     const __amdgpu_buffer_rsrc_t er =
         make_rsrc(ep, static_cast<uint32_t>(static_cast<int64_t>(a.M) * a.lde * 2));
@@ -399,22 +402,18 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
         float v[4] = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
                       acc[mi][ni][4 * g + 3]};
         uint2* slot = reinterpret_cast<uint2*>(ct.at(il, jl));
-        if (EPI == EPI_GRAM) {
+        if (EPI != EPI_SYMSQ) {
+          const float f = zero_unit ? 0.0f : s;  // a zero unit's update writes zeros
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = s * v[q];
-        } else if (!need_src) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = 0.0f;
+          for (int q = 0; q < 4; ++q) v[q] = f * v[q];
         } else {
           const uint2 w = *slot;
           const float e[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-          if (EPI == EPI_SYMSQ) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = a.cb * e[q] + a.cc * v[q];
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = s * (a.ca * e[q] + v[q]);
+          for (int q = 0; q < 4; ++q) {
+            v[q] = a.cb * e[q] + a.cc * v[q];
+            if (diag_tile && il == jl + q) v[q] += a.ca;
           }
         }
         uint2 w;
@@ -429,19 +428,25 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   });
   __syncthreads();
 
-  bf16_t* dst = uniform_ptr(reinterpret_cast<bf16_t*>(mat_at(a.dst, u)));
+  // Stores go through a buffer descriptor: 32-bit offsets (a unit is under
+  // 2 GiB), and a chunk outside the matrix gets an offset past the buffer's
+  // size, which the hardware drops.
+  const bf16_t* dst = uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.dst, u)));
+  const __amdgpu_buffer_rsrc_t dr =
+      make_rsrc(dst, static_cast<uint32_t>(static_cast<int64_t>(a.M) * a.ldd * 2));
+  const int ldd = static_cast<int>(a.ldd);
   const bool diag = (EPI != EPI_UPDATE) && ti == tj;
   constexpr int CH = BN / 8;  // 16-byte chunks per tile row
   // primary: C rows, 16-byte row-contiguous stores (a diagonal tile of a
   // symmetric output takes its lower half from the mirrored upper half)
-#pragma unroll 4
-  for (int e = tid; e < BM * CH; e += NT) {
+#pragma unroll
+  for (int it = 0; it < BM * CH / NT; ++it) {
+    const int e = tid + it * NT;
     const int rl = e / CH, c = e % CH;
     const int i = m0 + rl, j = n0 + 8 * c;
-    if (i >= a.M || j >= a.N) continue;
-    uint4 val;
+    u32x4_t val;
     if (!diag || 8 * c >= rl) {
-      val = *reinterpret_cast<const uint4*>(ct.at(rl, 8 * c));
+      val = *reinterpret_cast<const u32x4_t*>(ct.at(rl, 8 * c));
     } else {
       uint16_t h[8];
 #pragma unroll
@@ -450,15 +455,17 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
         h[q] = (cl >= rl) ? *reinterpret_cast<const uint16_t*>(ct.at(rl, cl))
                           : *reinterpret_cast<const uint16_t*>(ct.at(cl, rl));
       }
-      val = __builtin_bit_cast(uint4, h);
+      val = __builtin_bit_cast(u32x4_t, h);
     }
-    *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(i) * a.ldd + j) = val;
+    const uint32_t off = (i < a.M && j < a.N) ? static_cast<uint32_t>(i * ldd + j) * 2u : kOOB;
+    __builtin_amdgcn_raw_buffer_store_b128(val, dr, off, 0, 0);
   }
   if (EPI != EPI_UPDATE && !diag) {
     // mirror: row j of the output gets C[i .. i + 7][j] from two transposed
     // reads; blocks of 32 columns x 16 rows, one per wave at a time
     constexpr int BJ = BN / 32, BI = BM / 16;
     const int gq = lane >> 4, jx = lane & 15;
+#pragma unroll 4
     for (int b = wave; b < BJ * BI; b += NW) {
       const int jb = (b % BJ) * 32, ib = (b / BJ) * 16;
       const int col = jb + 16 * (gq & 1) + 4 * (jx & 3);
@@ -468,11 +475,10 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
       const int jl = jb + 16 * (gq & 1) + jx;  // column of C = output row
       const int il = ib + 8 * (gq >> 1);       // first of 8 rows of C = output column
       const int orow = n0 + jl, ocol = m0 + il;
-      if (orow < a.N && ocol < a.M) {
-        const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(orow) * a.ldd + ocol) =
-            __builtin_bit_cast(uint4, v);
-      }
+      const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const uint32_t off =
+          (orow < a.N && ocol < a.M) ? static_cast<uint32_t>(orow * ldd + ocol) * 2u : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), dr, off, 0, 0);
     }
   }
 }

@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void ns_gemm_simple_kernel(NsGemmArgs a) {
     if (a.scale_pow == 2) s = s * s;
   }
   T* dst = reinterpret_cast<T*>(mat_at(a.dst, u));
-  const T* ep = (EPI == EPI_GRAM) ? nullptr : reinterpret_cast<const T*>(mat_at(a.epi, u));
+  const T* ep = (EPI == EPI_SYMSQ) ? reinterpret_cast<const T*>(mat_at(a.epi, u)) : nullptr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int gi = m0 + ty * 4 + i;
@@ -100,9 +100,9 @@ __global__ __launch_bounds__(256) void ns_gemm_simple_kernel(NsGemmArgs a) {
         v = s * v;
       } else if (EPI == EPI_SYMSQ) {
         v = a.cb * muon::Elem<T>::load(ep + static_cast<int64_t>(gi) * a.lde + gj) + a.cc * v;
+        if (gi == gj) v += a.ca;
       } else {
-        v = zero_unit ? 0.0f
-                      : s * (a.ca * muon::Elem<T>::load(ep + static_cast<int64_t>(gi) * a.lde + gj) + v);
+        v = zero_unit ? 0.0f : s * v;
       }
       if (EPI == EPI_UPDATE) {
         muon::Elem<T>::store(dst + static_cast<int64_t>(gi) * a.ldd + gj, v);

@@ -8,7 +8,7 @@
 // Per call: `units` Newton-Schulz units of ur x uc (m = min, n = max).
 // Regions (byte offsets into the workspace, 256-byte aligned):
 //   xa, xb   two m*n iterate buffers        (ping-pong)
-//   a, b     two m*m buffers                (A = X X^T, B = bA + cA^2)
+//   a, b     two m*m buffers                (A = X X^T, B' = aI + bA + cA^2)
 //   scale    float per unit                 1 / (||Y||_F + eps)
 //   zflag    int per unit                   ||Y||_F == 0
 //   partial  double per unit and part       norm partial sums
