@@ -47,14 +47,20 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4_ptr_t;
 
 namespace {
 
-constexpr int BK = 64;                 // bf16 elements of K per stage
 constexpr uint32_t kOOB = 0x80000000u; // buffer offset past any matrix: loads return 0
 constexpr int kRsrcWord3 = 0x00020000; // raw buffer, 32-bit data format (gfx9 family)
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8; a field at its maximum does not wait.
+constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
+}
 
 // A pointer every lane holds the same value of, moved to scalar registers
 // (buffer descriptors need it; a value read from a device table is not known
@@ -77,6 +83,25 @@ __device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& r, char* lds
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
 }
 
+// The same 16-byte global -> LDS load for the operand stages, written as
+// inline asm on a descriptor held as four words.  The compiler then does not
+// track these LDS writes: the k-loop orders them itself (s_waitcnt vmcnt
+// before each barrier), and no conservative wait for the most recent load is
+// inserted ahead of LDS reads of other stage buffers.  M0 holds the LDS
+// destination of the wave's 1 KiB block.
+__device__ __forceinline__ u32x4_t rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  return u32x4_t{static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32) & 0xffffu, bytes,
+                 static_cast<uint32_t>(kRsrcWord3)};
+}
+__device__ __forceinline__ void dma16_asm(const u32x4_t& r, char* lds, uint32_t voff,
+                                          uint32_t soff) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
+  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff),
+               "{m0}"(m0)
+               : "memory");
+}
+
 // Four consecutive k of one column of a row-major [k][col] LDS tile per lane
 // (ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
 // i % 4 of the 8-byte words addressed by lanes i / 4 + 4 r, r = 0..3).
@@ -84,10 +109,18 @@ __device__ __forceinline__ i16x4_t ld_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr_t)(p));
 }
 
-// ---- K-contiguous operand tile: R rows x BK, 128-byte rows, chunk swizzle
-// (row ^ row >> 3) & 7 keeps the 16 rows an LDS cycle serves on distinct banks.
+// ---- K-contiguous operand tile: R rows x BK (= 64), 128-byte rows of
+// 16-byte chunks.  The chunk swizzle chunk ^ (row ^ row >> 3) & 7 puts the
+// 16 rows one LDS cycle of a fragment read serves (same logical chunk,
+// consecutive rows) on distinct banks.
+template <int BK>
+__device__ __forceinline__ int rt_swz(int row) {
+  static_assert(BK == 64, "swizzle laid out for 64-element rows");
+  return (row ^ (row >> 3)) & 7;
+}
+template <int BK>
 __device__ __forceinline__ int rt_off(int row, int chunk) {
-  return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+  return row * (2 * BK) + ((chunk ^ rt_swz<BK>(row)) << 4);
 }
 
 // ---- K-major operand tile: BK rows (k) x R columns, 2R-byte rows, chunk
@@ -98,24 +131,29 @@ __device__ __forceinline__ int kt_off(int k, int col) {
   return k * (2 * R) + (((col >> 3) ^ ((k & 3) << 2)) << 4) + ((col & 7) << 1);
 }
 
-template <int R, bool KMAJOR, int NW>
+template <int R, bool KMAJOR, int NW, int BK>
 struct Operand;
 
-template <int R, int NW>
-struct Operand<R, false, NW> {
-  static constexpr int NG = R / (8 * NW);  // 8 rows per wave instruction
+template <int R, int NW, int BK>
+struct Operand<R, false, NW, BK> {
+  static constexpr int CPR = BK / 8;          // 16-byte chunks per tile row
+  static constexpr int RPI = 64 / CPR;        // tile rows per wave instruction
+  static constexpr int NG = R / (RPI * NW);   // instructions per wave per stage
   uint32_t base[NG];
   int kc[NG];
-  __amdgpu_buffer_rsrc_t rsrc;
+  u32x4_t rsrc;
 
-  // src: rows x ld matrix; tile rows [row0, row0 + R).
+  // src: rows x ld matrix; tile rows [row0, row0 + R).  Lane l of an
+  // instruction fills LDS bytes 16 l .. 16 l + 15 of its 1 KiB block, i.e.
+  // physical chunk l % CPR of row l / CPR, which holds the logical chunk
+  // that the swizzle maps there.
   __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int rows, int /*K*/,
                                        int row0, int wave, int lane) {
-    rsrc = make_rsrc(src, static_cast<uint32_t>(static_cast<int64_t>(rows) * ld * 2));
+    rsrc = rsrc_words(src, static_cast<uint32_t>(static_cast<int64_t>(rows) * ld * 2));
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
-      const int row = 8 * (wave + NW * q) + (lane >> 3);
-      const int lc = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+      const int row = RPI * (wave + NW * q) + lane / CPR;
+      const int lc = (lane % CPR) ^ rt_swz<BK>(row);
       const int gr = row0 + row;
       kc[q] = 8 * lc;
       base[q] = (gr < rows) ? static_cast<uint32_t>((static_cast<int64_t>(gr) * ld + 8 * lc) * 2)
@@ -127,27 +165,27 @@ struct Operand<R, false, NW> {
     const uint32_t soff = static_cast<uint32_t>(k0 * 2);
 #pragma unroll
     for (int q = 0; q < NG; ++q)
-      dma16(rsrc, lds + (wave + NW * q) * 1024, (full || k0 + kc[q] < K) ? base[q] : kOOB, soff);
+      dma16_asm(rsrc, lds + (wave + NW * q) * 1024, (full || k0 + kc[q] < K) ? base[q] : kOOB, soff);
   }
   // MFMA operand for tile rows rb .. rb + 31, k = 16 kk + 8 (lane / 32) + 0..7
   __device__ __forceinline__ bf16x8_t frag(const char* t, int rb, int kk, int lane) const {
-    return *reinterpret_cast<const bf16x8_t*>(t + rt_off(rb + (lane & 31), 2 * kk + (lane >> 5)));
+    return *reinterpret_cast<const bf16x8_t*>(t + rt_off<BK>(rb + (lane & 31), 2 * kk + (lane >> 5)));
   }
 };
 
-template <int R, int NW>
-struct Operand<R, true, NW> {
+template <int R, int NW, int BK>
+struct Operand<R, true, NW, BK> {
   static constexpr int CPR = R / 8;         // 16-byte chunks per tile row
   static constexpr int RPI = 64 / CPR;      // tile rows per wave instruction
-  static constexpr int NG = BK / RPI / NW;  // instructions per wave
+  static constexpr int NG = BK / RPI / NW;  // instructions per wave per stage
   uint32_t base[NG];
   int kr[NG];
-  __amdgpu_buffer_rsrc_t rsrc;
+  u32x4_t rsrc;
 
   // src: K x ld matrix (k = memory row); tile columns [col0, col0 + R).
   __device__ __forceinline__ void init(const bf16_t* src, int64_t ld, int cols, int K, int col0,
                                        int wave, int lane) {
-    rsrc = make_rsrc(src, static_cast<uint32_t>(static_cast<int64_t>(K) * ld * 2));
+    rsrc = rsrc_words(src, static_cast<uint32_t>(static_cast<int64_t>(K) * ld * 2));
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       const int k = RPI * (wave + NW * q) + lane / CPR;
@@ -163,15 +201,15 @@ struct Operand<R, true, NW> {
     const uint32_t soff = static_cast<uint32_t>(static_cast<int64_t>(k0) * ld * 2);
 #pragma unroll
     for (int q = 0; q < NG; ++q)
-      dma16(rsrc, lds + (wave + NW * q) * 1024, (full || k0 + kr[q] < K) ? base[q] : kOOB, soff);
+      dma16_asm(rsrc, lds + (wave + NW * q) * 1024, (full || k0 + kr[q] < K) ? base[q] : kOOB, soff);
   }
   __device__ __forceinline__ bf16x8_t frag(const char* t, int rb, int kk, int lane) const {
     const int gq = lane >> 4, j = lane & 15;
     const int col = rb + 16 * (gq & 1) + 4 * (j & 3);
     const int k = 16 * kk + 8 * (gq >> 1) + (j >> 2);
-    const i16x4_t lo = ld_tr16(t + kt_off<R>(k, col));
-    const i16x4_t hi = ld_tr16(t + kt_off<R>(k + 4, col));
-    const short v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const u32x2_t lo = __builtin_bit_cast(u32x2_t, ld_tr16(t + kt_off<R>(k, col)));
+    const u32x2_t hi = __builtin_bit_cast(u32x2_t, ld_tr16(t + kt_off<R>(k + 4, col)));
+    const u32x4_t v = {lo.x, lo.y, hi.x, hi.y};
     return __builtin_bit_cast(bf16x8_t, v);
   }
 };
@@ -185,14 +223,18 @@ __device__ __forceinline__ int ct_off(int row, int col) {
   return row * (2 * BN) + (((col >> 3) ^ g) << 4) + ((col & 7) << 1);
 }
 
-// The staged tile spans both stage buffers: rows [0, BM / 2) in the first,
-// the rest in the second.
-template <int BM, int BN>
+// The staged tile spans NP of the stage buffers, BM / NP rows in each.
+template <int BM, int BN, int NP>
 struct OutTile {
-  char* lo;
-  char* hi;
+  char* p[4];
+  __device__ __forceinline__ char* part(int q) const {
+    if (NP == 1) return p[0];
+    if (NP == 2) return q ? p[1] : p[0];
+    return q < 2 ? (q ? p[1] : p[0]) : (q == 3 ? p[3] : p[2]);
+  }
   __device__ __forceinline__ char* at(int row, int col) const {
-    return row < BM / 2 ? lo + ct_off<BN>(row, col) : hi + ct_off<BN>(row - BM / 2, col);
+    constexpr int RP = BM / NP;
+    return part(row / RP) + ct_off<BN>(row % RP, col);
   }
 };
 
@@ -206,19 +248,37 @@ template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
+template <int V>
+using ic = std::integral_constant<int, V>;
 
-template <int BM, int BN, int NWN, bool TM, bool TN, int EPI>
+template <int BM, int BN, int NWN, int BK, int NS, bool TM, bool TN, int EPI>
 __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a) {
   constexpr int NW = 2 * NWN, NT = 64 * NW;  // waves: 2 along M x NWN along N
   constexpr int WM = BM / 2, WN = BN / NWN;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int STAGE = (BM + BN) * BK * 2;
-  static_assert(2 * STAGE >= BM * BN * 2, "output tile must fit the stage buffers");
-  // Two distinct LDS objects for the two stages: the DMA writes into one are
-  // then provably disjoint from the reads of the other, so no wait on the
-  // loads in flight is inserted ahead of the MFMA loop.
-  __shared__ __attribute__((aligned(1024))) char stage0[STAGE];
-  __shared__ __attribute__((aligned(1024))) char stage1[STAGE];
+  constexpr int NP = (BM * BN * 2 + STAGE - 1) / STAGE;  // stage buffers the output tile spans
+  // NS stage buffers, NS - 1 stages in flight.  Only NS = 2 with BK = 64 is
+  // instantiated: a four-buffer ring of BK = 32 stages (three in flight)
+  // measured slower on gfx950, its extra barrier per 32 k costing more than
+  // the deeper prefetch gains.
+  static_assert(NS == 2 && BK == 64, "two stage buffers of 64 k");
+  static_assert(NP <= NS && (NP & (NP - 1)) == 0 && STAGE >= (BM / NP) * BN * 2,
+                "output tile must fit the stage buffers");
+  // Distinct LDS objects per stage: the DMA writes into one are then provably
+  // disjoint from the reads of the others, so no wait on the loads in flight
+  // is inserted ahead of the MFMAs.
+  __shared__ __attribute__((aligned(1024))) char st0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) char st3[NS > 2 ? STAGE : 16];
+  auto buf = [&](auto I) -> char* {
+    constexpr int i = decltype(I)::value % NS;
+    if constexpr (i == 0) return st0;
+    else if constexpr (i == 1) return st1;
+    else if constexpr (i == 2) return st2;
+    else return st3;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -254,8 +314,10 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
     for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = (f32x16_t)(0.0f);
 
   if (!zero_unit) {
-    Operand<BM, TM, NW> om;
-    Operand<BN, TN, NW> on;
+    using OpM = Operand<BM, TM, NW, BK>;
+    using OpN = Operand<BN, TN, NW, BK>;
+    OpM om;
+    OpN on;
     om.init(uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.pm, u))), a.ldm, a.M, a.K, m0,
             wave, lane);
     on.init(uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.pn, u))), a.ldn, a.N, a.K, n0,
@@ -267,6 +329,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
       om.issue(st, kt * BK, a.K, a.ldm, wave, full);
       on.issue(st + BM * BK * 2, kt * BK, a.K, a.ldn, wave, full);
     };
+    constexpr int NL = OpM::NG + OpN::NG;  // load instructions per wave per stage
 
     // Register double buffer of MFMA fragments: the LDS reads of k16 step
     // kk + 1 are issued among the MFMAs of step kk.
@@ -287,6 +350,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][ni], fb[b][mi], acc[mi][ni], 0, 0, 0);
       });
     };
+    constexpr int KK = BK / 16;                                      // k16 steps per stage
     constexpr int NMF = FM * FN;                                     // MFMAs per k16 step
     constexpr int NRD = (TN ? 2 : 1) * FN + (TM ? 2 : 1) * FM;       // LDS reads per k16 step
     constexpr int TAIL = NMF / 2;                                    // MFMAs after the barrier
@@ -299,51 +363,46 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
       });
     };
 
-    // One stage in buffer `cur` (its k16-step-0 fragments already in fa/fb[0]);
-    // the next stage sits in `nxt`; after the barrier, the stage two ahead is
-    // loaded into `cur`.
-    auto stage = [&](const char* cur, const char* nxt, char* cur_w, int kt_next2) {
-      static_for<BK / 16>([&](auto KK) {
-        constexpr int kk = decltype(KK)::value;
+    // Stage kt in buffer kt % NS (its first fragments already in registers).
+    // Near its end: wait until this wave's loads of stage kt + 1 have landed
+    // (the NS - 2 later stages may still fly) and this wave's reads of stage
+    // kt are done; the barrier then makes stage kt + 1 visible and frees
+    // buffer kt % NS, which receives stage kt + NS.
+    auto stage = [&](auto S, int kt_new) {
+      char* cur = buf(S);
+      const char* nxt = buf(ic<decltype(S)::value + 1>{});
+      static_for<KK>([&](auto KI) {
+        constexpr int kk = decltype(KI)::value;
         constexpr int b = kk & 1;
-        if constexpr (kk + 1 < BK / 16) {
-          frags(cur, kk + 1, std::integral_constant<int, b ^ 1>{});
-          mfmas(std::integral_constant<int, b>{}, std::integral_constant<int, 0>{},
-                std::integral_constant<int, NMF>{});
-          interleave(std::integral_constant<int, NMF>{});
+        if constexpr (kk + 1 < KK) {
+          frags(cur, kk + 1, ic<b ^ 1>{});
+          mfmas(ic<b>{}, ic<0>{}, ic<NMF>{});
+          interleave(ic<NMF>{});
           __builtin_amdgcn_sched_barrier(0);
         } else {
-          mfmas(std::integral_constant<int, b>{}, std::integral_constant<int, 0>{},
-                std::integral_constant<int, NMF - TAIL>{});
+          mfmas(ic<b>{}, ic<0>{}, ic<NMF - TAIL>{});
           __builtin_amdgcn_sched_barrier(0);
-          // every read of `cur` done, this wave's loads of the next stage done
-          asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-          __syncthreads();
-          issue(cur_w, kt_next2);
+          // a bare s_barrier: __syncthreads() adds a workgroup fence, which
+          // would also wait for the loads still meant to be in flight
+          asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"((NS - 2) * NL) : "memory");
+          issue(cur, kt_new);
           __builtin_amdgcn_sched_barrier(0);
-          frags(nxt, 0, std::integral_constant<int, 0>{});
-          mfmas(std::integral_constant<int, b>{}, std::integral_constant<int, NMF - TAIL>{},
-                std::integral_constant<int, NMF>{});
-          interleave(std::integral_constant<int, TAIL>{});
+          frags(nxt, 0, ic<0>{});
+          mfmas(ic<b>{}, ic<NMF - TAIL>{}, ic<NMF>{});
+          interleave(ic<TAIL>{});
           __builtin_amdgcn_sched_barrier(0);
         }
       });
     };
 
-    // Stage kt + 1 loads while stage kt computes; it is issued at the barrier
-    // near the end of stage kt - 1, once every wave has finished reading the
-    // buffer it overwrites.  Even stages live in stage0, odd in stage1 (two
-    // fixed LDS objects, loop unrolled by two).  The loop runs whole pairs:
-    // stages at or past K load zeros (offsets fall outside the buffer), so
-    // the body has no branches.
-    issue(stage0, 0);
-    issue(stage1, 1);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    frags(stage0, 0, std::integral_constant<int, 0>{});
-    for (int kt = 0; kt < KT; kt += 2) {
-      stage(stage0, stage1, stage0, kt + 2);
-      stage(stage1, stage0, stage1, kt + 3);
+    // The first NS stages load up front; the loop runs whole rounds of NS
+    // stages (fixed LDS objects, no branches): stages at or past K load
+    // zeros (offsets fall outside the buffer) and add nothing.
+    static_for<NS>([&](auto S) { issue(buf(S), decltype(S)::value); });
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" :: "n"((NS - 1) * NL) : "memory");
+    frags(buf(ic<0>{}), 0, ic<0>{});
+    for (int kt = 0; kt < KT; kt += NS) {
+      static_for<NS>([&](auto S) { stage(S, kt + decltype(S)::value + NS); });
     }
   }
 
@@ -358,37 +417,42 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   }
   // every wave is done reading the operand stages, and the (zero-filled)
   // loads the last k-stages issued past K have landed
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
   __syncthreads();
-  static_assert(STAGE >= (BM / 2) * BN * 2, "half of the output tile per stage buffer");
-  const OutTile<BM, BN> ct{stage0, stage1};
-  // symsq adds b A: fetch that tile of A into the staging area with one round
-  // of global->LDS loads, laid out exactly like the output tile, and finish
-  // the values in place.
+  OutTile<BM, BN, NP> ct;
+  ct.p[0] = buf(ic<0>{});
+  ct.p[1] = buf(ic<1>{});
+  ct.p[2] = buf(ic<2 % NS>{});
+  ct.p[3] = buf(ic<3 % NS>{});
   const bool diag_tile = ti == tj;
   if (EPI == EPI_SYMSQ) {
+    // symsq adds b A: fetch that tile of A into the staging area with one
+    // round of global->LDS loads, laid out exactly like the output tile, and
+    // finish the values in place.
     const bf16_t* ep = uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.epi, u)));
     const __amdgpu_buffer_rsrc_t er =
         make_rsrc(ep, static_cast<uint32_t>(static_cast<int64_t>(a.M) * a.lde * 2));
-    constexpr int RB = 2 * BN;                 // bytes per staged row
-    constexpr int HALF = (BM / 2) * RB / 1024; // wave instructions per half tile
+    constexpr int RB = 2 * BN;                   // bytes per staged row
+    constexpr int RP = BM / NP;                  // rows per part
+    constexpr int IPP = RP * RB / 1024;          // wave instructions per part
+    static_assert(IPP * 1024 == RP * RB && (NP * IPP) % NW == 0, "staging split");
 #pragma unroll
-    for (int q = 0; q < 2 * HALF / NW; ++q) {
+    for (int q = 0; q < NP * IPP / NW; ++q) {
       const int g = wave + NW * q;
-      const int h = g >= HALF;                 // which stage buffer
-      const int pos = (g - h * HALF) * 1024 + lane * 16;
-      const int rl = pos / RB;                 // row within the half
-      const int pc = (pos % RB) >> 4;          // physical chunk
+      const int h = g / IPP;                     // which part
+      const int pos = (g - h * IPP) * 1024 + lane * 16;
+      const int rl = pos / RB;                   // row within the part
+      const int pc = (pos % RB) >> 4;            // physical chunk
       const int gsw = ((rl & 3) << 2) | ((rl >> 2) & 3);
-      const int row = rl + h * (BM / 2);
+      const int row = rl + h * RP;
       const int col = 8 * (pc ^ gsw);
       const int gi = m0 + row, gj = n0 + col;
       const uint32_t off = (gi < a.M && gj < a.N)
                                ? static_cast<uint32_t>((static_cast<int64_t>(gi) * a.lde + gj) * 2)
                                : kOOB;
-      dma16(er, (h ? stage1 : stage0) + (g - h * HALF) * 1024, off, 0);
+      dma16(er, ct.part(h) + (g - h * IPP) * 1024, off, 0);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     __syncthreads();
   }
   static_for<FM>([&](auto MI) {
@@ -435,7 +499,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   const __amdgpu_buffer_rsrc_t dr =
       make_rsrc(dst, static_cast<uint32_t>(static_cast<int64_t>(a.M) * a.ldd * 2));
   const int ldd = static_cast<int>(a.ldd);
-  const bool diag = (EPI != EPI_UPDATE) && ti == tj;
+  const bool diag = (EPI != EPI_UPDATE) && diag_tile;
   constexpr int CH = BN / 8;  // 16-byte chunks per tile row
   // primary: C rows, 16-byte row-contiguous stores (a diagonal tile of a
   // symmetric output takes its lower half from the mirrored upper half)
@@ -485,12 +549,14 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
 
 template <int T, bool TM, bool TN, int EPI>
 hipError_t go(hipStream_t s, const NsGemmArgs& a) {
-  // 256 x 256 tiles: 8 waves (two per SIMD) of 128 x 64; 128 x 128: 4 waves of 64 x 64
+  // 256 x 256 tiles: 8 waves (two per SIMD) of 128 x 64; 128 x 128: 4 waves
+  // of 64 x 64.  BK = 64, two stage buffers.
   constexpr int NWN = T == 256 ? 4 : 2;
+  constexpr int BK = 64, NS = 2;
   const int64_t grid = a.units * a.tiles_per_unit;
   if (grid <= 0) return hipSuccess;
   if (grid > 0x7fffffffLL / 512) return hipErrorInvalidValue;
-  ns_gemm_mfma_kernel<T, T, NWN, TM, TN, EPI><<<static_cast<unsigned>(grid), 128 * NWN, 0, s>>>(a);
+  ns_gemm_mfma_kernel<T, T, NWN, BK, NS, TM, TN, EPI><<<static_cast<unsigned>(grid), 128 * NWN, 0, s>>>(a);
   return hipGetLastError();
 }
 

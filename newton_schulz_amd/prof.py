@@ -70,6 +70,7 @@ def traffic(a):
     sf = a.copy_bytes / (cf / ncf * 1024.0)
     sw = a.copy_bytes / (cw / ncw * 1024.0)
     res = {
+        "kernel": a.label or a.kernel,
         "kernel_match": a.kernel,
         "dispatches": nf,
         "fetch_kib_per_dispatch": f / nf,
@@ -103,6 +104,7 @@ def main(argv=None):
     t.add_argument("--copy-kernel", default="copy")
     t.add_argument("--kernel", required=True)
     t.add_argument("--source", default=None, help="kernel source file to fingerprint")
+    t.add_argument("--label", default=None, help="kernel description stored in the record")
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         stats(a.csv)
