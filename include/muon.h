@@ -44,6 +44,23 @@ typedef enum {
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
 
+/* How the iteration is evaluated (the DeepSpeed PR "[Muon] CPU offload: pin
+ * the momentum and overlap the host writeback", section Tests, and the RFC's
+ * section 5 Roadmap name an ns_method option with a "gram" choice beside the
+ * standard one; neither page spells gram out).
+ *   MUON_NS_QUINTIC: the iteration below on the m x n iterate, step by step.
+ *   MUON_NS_GRAM:    the same polynomial map carried on m x m matrices only.
+ *     With A_0 = X_0 X_0^T and P_k = a I + b A_k + c A_k^2 (a polynomial in
+ *     A_k, so symmetric and commuting with it), X_{k+1} = P_k X_k gives
+ *     A_{k+1} = P_k A_k P_k and X_steps = (P_{steps-1} ... P_0) X_0.  The
+ *     m x n matrix is read twice (A_0 and the final product) instead of three
+ *     times per step; every other product is m x m.  The result equals the
+ *     quintic's in exact arithmetic; bf16 rounding differs.  A_0 carries the
+ *     squared singular values, which bf16 resolves only when the matrix is
+ *     far from square: in BF16 compute the Gram form runs on units with
+ *     2 m <= n and the quintic iteration on the others (F32: always). */
+typedef enum { MUON_NS_QUINTIC = 0, MUON_NS_GRAM = 1 } muon_ns_method_t;
+
 /* Newton-Schulz parameters.  The quintic iteration is the one the DeepSpeed
  * RFC "Enable Correct and High-Performance Muon Optimizer under ZeRO CPU
  * Offload" calls the current default (section 5, Roadmap), run for 5~6
@@ -61,6 +78,7 @@ typedef struct {
   float eps;         /* added to the Frobenius norm, >= 0 */
   int32_t compute;   /* muon_dtype_t: BF16 = bf16 MFMA with fp32 accumulate,
                         F32 = fp32 verification mode */
+  int32_t method;    /* muon_ns_method_t, default MUON_NS_QUINTIC */
 } muon_ns_params_t;
 
 /* Geometry of one weight matrix (RFC section 4A: keep the 2D shape and head
@@ -222,7 +240,8 @@ typedef enum {
   MUON_K_SYMSQ = 3,
   MUON_K_UPDATE = 4,
   MUON_K_APPLY = 5,
-  MUON_K_COUNT = 6
+  MUON_K_PROD = 6,   /* m x m products of MUON_NS_GRAM (P_k Q_k, P_k A_k, (P_k A_k) P_k) */
+  MUON_K_COUNT = 7
 } muon_kernel_class_t;
 
 muon_status_t muon_timing_enable(muon_ctx_t* ctx, int32_t enable, int32_t capacity);

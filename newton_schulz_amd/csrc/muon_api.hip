@@ -119,6 +119,7 @@ void muon_ns_params_default(muon_ns_params_t* p) {
   p->c = 2.0315f;
   p->eps = 1e-7f;
   p->compute = MUON_BF16;
+  p->method = MUON_NS_QUINTIC;
 }
 
 size_t muon_ctx_workspace_bytes(const muon_ctx_t* ctx) { return ctx ? ctx->ws_bytes : 0; }
@@ -327,6 +328,8 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   if (io_dtype != prm->compute)
     return fail(c, MUON_EDTYPE, "io dtype must equal the compute dtype");
   if (prm->steps < 0 || !(prm->eps >= 0.0f)) return fail(c, MUON_EINVAL, "steps/eps");
+  if (prm->method != MUON_NS_QUINTIC && prm->method != MUON_NS_GRAM)
+    return fail(c, MUON_EINVAL, "method");
   NsLayout L;
   if (!ns_layout(shape, count, prm->compute, &L)) return fail(c, MUON_ESHAPE, "shape");
   if (count == 0) return MUON_OK;
@@ -403,6 +406,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     a.tiles_n = static_cast<int>((a.N + T - 1) / T);
     a.tiles_per_unit = (epi == EPI_UPDATE) ? a.tiles_m * a.tiles_n : a.tiles_m * (a.tiles_m + 1) / 2;
     a.units = L.units;
+    a.cus = c->cus;
     a.zflag = zflag;
     a.ca = prm->a;
     a.cb = prm->b;
@@ -441,6 +445,100 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     tstop(c, s, k);
     return r;
   };
+  // The Gram form squares the singular values into A_0; in bf16 that loses
+  // the small ones once m nears n (relative error ~1e-1 on square Gaussian
+  // inputs against ~1e-2 for the quintic), so bf16 runs it only on units with
+  // 2 m <= n, where its error stays at the quintic's level.
+  const bool gram_form =
+      prm->method == MUON_NS_GRAM && (prm->compute == MUON_F32 || 2 * m <= n);
+  if (gram_form) {
+    // m x m matrices live in A, B and (at m x m stride) the two iterate
+    // regions; the input is read by the first and the last product only.
+    const MatRef R2{ws + L.xa, abytes, nullptr}, R3{ws + L.xb, abytes, nullptr};
+    auto sym_prod = [&](int cls, const MatRef& p, const MatRef& q, const MatRef& d) {
+      // d = p q for symmetric commuting p, q: the Gram product p q^T, upper tiles
+      NsGemmArgs pa{};
+      pa.pm = p; pa.pn = q; pa.dst = d; pa.epi = d;
+      pa.ldm = pa.ldn = pa.ldd = pa.lde = m;
+      pa.M = pa.N = pa.K = static_cast<int>(m);
+      return gemm(cls, pa, EPI_GRAM, false, false);
+    };
+    NsGemmArgs ga{};
+    ga.pm = in.ref; ga.pn = in.ref; ga.dst = AR; ga.epi = AR;
+    ga.ldm = ga.ldn = tall ? m : n;
+    ga.ldd = ga.lde = m;
+    ga.M = ga.N = static_cast<int>(m);
+    ga.K = static_cast<int>(n);
+    ga.scale = scale;
+    ga.scale_pow = 2;
+    e = gemm(MUON_K_GRAM, ga, EPI_GRAM, tall, tall);
+    if (e != hipSuccess) return hip_fail(c, e, "gram launch");
+    MatRef Q = R2, other = R3;
+    for (int k = 0; k < prm->steps; ++k) {
+      // P_k = a I + b A_k + c A_k^2; P_0 is Q_1 itself
+      const MatRef P = (k == 0) ? R2 : BR;
+      NsGemmArgs sa{};
+      sa.pm = AR; sa.pn = AR; sa.dst = P; sa.epi = AR;
+      sa.ldm = sa.ldn = sa.ldd = sa.lde = m;
+      sa.M = sa.N = sa.K = static_cast<int>(m);
+      e = gemm(MUON_K_SYMSQ, sa, EPI_SYMSQ, false, false);
+      if (e != hipSuccess) return hip_fail(c, e, "symsq launch");
+      if (k > 0) {
+        e = sym_prod(MUON_K_PROD, P, Q, other);  // Q_{k+1} = P_k Q_k
+        if (e != hipSuccess) return hip_fail(c, e, "product launch");
+        std::swap(Q, other);
+      }
+      if (k + 1 < prm->steps) {
+        // A_{k+1} = (P_k A_k) P_k, through the free region
+        e = sym_prod(MUON_K_PROD, P, AR, other);
+        if (e == hipSuccess) e = sym_prod(MUON_K_PROD, other, P, AR);
+        if (e != hipSuccess) return hip_fail(c, e, "product launch");
+      }
+    }
+    // X = s Q X_0 (tall: Y Q).  Written straight to the output unless the
+    // output overlaps the input, then through the free iterate region.
+    const int64_t call_bytes = unit_bytes * per;
+    const char *ilo = nullptr, *ihi = nullptr, *olo = nullptr, *ohi = nullptr;
+    bool alias = false;
+    for (int64_t i = 0; i < count; ++i) {
+      const char* pi = static_cast<const char*>(mats[i]);
+      const char* po = static_cast<const char*>(outp[i]);
+      alias = alias || pi == po;
+      ilo = (i == 0 || pi < ilo) ? pi : ilo;
+      ihi = (i == 0 || pi + call_bytes > ihi) ? pi + call_bytes : ihi;
+      olo = (i == 0 || po < olo) ? po : olo;
+      ohi = (i == 0 || po + call_bytes > ohi) ? po + call_bytes : ohi;
+    }
+    alias = alias || ranges_overlap(ilo, ihi - ilo, olo, ohi - olo);
+    const MatRef freeX = (Q.base == R2.base) ? XB : XA;
+    NsGemmArgs ua{};
+    ua.dst = alias ? freeX : ot.ref;
+    ua.scale = scale;
+    ua.scale_pow = 1;
+    ua.zero_write = 1;
+    if (!tall) {
+      ua.pm = Q; ua.ldm = m;
+      ua.pn = in.ref; ua.ldn = n;
+      ua.ldd = ua.lde = n;
+      ua.M = static_cast<int>(m);
+      ua.N = static_cast<int>(n);
+    } else {
+      ua.pm = in.ref; ua.ldm = m;
+      ua.pn = Q; ua.ldn = m;
+      ua.ldd = ua.lde = m;
+      ua.M = static_cast<int>(n);
+      ua.N = static_cast<int>(m);
+    }
+    ua.K = static_cast<int>(m);
+    e = gemm(MUON_K_UPDATE, ua, EPI_UPDATE, false, !tall);
+    if (e != hipSuccess) return hip_fail(c, e, "update launch");
+    if (alias) {
+      e = launch_scale_copy(s, freeX, ot.ref, unit_elems, L.units, nullptr, io_bf16);
+      if (e != hipSuccess) return hip_fail(c, e, "copy launch");
+    }
+    return MUON_OK;
+  }
+
   for (int k = 0; k < prm->steps; ++k) {
     const bool last = (k == prm->steps - 1);
     const MatRef src = (k == 0) ? in.ref : (((k - 1) % 2 == 0) ? XA : XB);

@@ -25,6 +25,7 @@ struct NsGemmArgs {
   int M, N, K;
   int tiles_m, tiles_n, tiles_per_unit;
   int64_t units;
+  int cus;             // compute units of the device (persistent grid size)
   const float* scale;  // per-unit normalisation factor s, or nullptr
   int scale_pow;       // 0: not applied, 1: multiply by s, 2: by s*s
   const int* zflag;    // per-unit "norm is zero" flag, or nullptr

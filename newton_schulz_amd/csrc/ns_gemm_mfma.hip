@@ -285,7 +285,20 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / NWN, wn = wave % NWN;
 
-  const int64_t lid = xcd_logical_id(blockIdx.x, gridDim.x);
+  // Persistent tiles: workgroup hw runs on XCD hw % 8 (round-robin dispatch,
+  // each XCD with its own L2).  XCD x owns one contiguous run of tiles,
+  // shared among its cnt workgroups in strides of cnt, so at any moment the
+  // workgroups of an XCD work on neighbouring tiles.  A workgroup moves on to
+  // its next tile without leaving the CU: the loads of the next tile start
+  // while the stores of the last one drain.
+  const int64_t total = a.units * a.tiles_per_unit;
+  const int G = static_cast<int>(gridDim.x), hw = static_cast<int>(blockIdx.x);
+  const int xg = hw % 8, q8 = G / 8, r8 = G % 8;
+  const int cnt = q8 + (xg < r8 ? 1 : 0);
+  const int64_t P = static_cast<int64_t>(xg) * q8 + min(xg, r8);
+  const int64_t t_end = total * (P + cnt) / G;
+
+  for (int64_t lid = total * P / G + hw / 8; lid < t_end; lid += cnt) {
   const int64_t u = lid / a.tiles_per_unit;
   const int t = static_cast<int>(lid - u * a.tiles_per_unit);
   int ti, tj;
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   const int m0 = ti * BM, n0 = tj * BN;
 
   const bool zero_unit = a.zflag != nullptr && a.zflag[u] != 0;
-  if (zero_unit && !(EPI == EPI_UPDATE && a.zero_write)) return;
+  if (zero_unit && !(EPI == EPI_UPDATE && a.zero_write)) continue;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -407,6 +420,12 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   }
 
   // ---- epilogue: finish values in registers, stage bf16 tile in LDS, store.
+  // Its LDS and global addresses depend on the lane only; an opaque copy of
+  // the lane index keeps the compiler from hoisting them out of the tile loop,
+  // where they would hold registers through the k-loop.
+  int elane = lane;
+  asm volatile("" : "+v"(elane));
+  const int etid = wave * 64 + elane;
   // MFMA operand A carried the N side, so lane l holds local row
   // wm WM + mi 32 + l % 32 of C and, per register group g, four consecutive
   // local columns wn WN + ni 32 + 8 g + 4 (l / 32) + 0..3.
@@ -440,7 +459,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
     for (int q = 0; q < NP * IPP / NW; ++q) {
       const int g = wave + NW * q;
       const int h = g / IPP;                     // which part
-      const int pos = (g - h * IPP) * 1024 + lane * 16;
+      const int pos = (g - h * IPP) * 1024 + elane * 16;
       const int rl = pos / RB;                   // row within the part
       const int pc = (pos % RB) >> 4;            // physical chunk
       const int gsw = ((rl & 3) << 2) | ((rl >> 2) & 3);
@@ -457,12 +476,12 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   }
   static_for<FM>([&](auto MI) {
     constexpr int mi = decltype(MI)::value;
-    const int il = wm * WM + mi * 32 + (lane & 31);
+    const int il = wm * WM + mi * 32 + (elane & 31);
     static_for<FN>([&](auto NI) {
       constexpr int ni = decltype(NI)::value;
       static_for<4>([&](auto G) {
         constexpr int g = decltype(G)::value;
-        const int jl = wn * WN + ni * 32 + 8 * g + 4 * (lane >> 5);
+        const int jl = wn * WN + ni * 32 + 8 * g + 4 * (elane >> 5);
         float v[4] = {acc[mi][ni][4 * g + 0], acc[mi][ni][4 * g + 1], acc[mi][ni][4 * g + 2],
                       acc[mi][ni][4 * g + 3]};
         uint2* slot = reinterpret_cast<uint2*>(ct.at(il, jl));
@@ -505,7 +524,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   // symmetric output takes its lower half from the mirrored upper half)
 #pragma unroll
   for (int it = 0; it < BM * CH / NT; ++it) {
-    const int e = tid + it * NT;
+    const int e = etid + it * NT;
     const int rl = e / CH, c = e % CH;
     const int i = m0 + rl, j = n0 + 8 * c;
     u32x4_t val;
@@ -528,7 +547,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
     // mirror: row j of the output gets C[i .. i + 7][j] from two transposed
     // reads; blocks of 32 columns x 16 rows, one per wave at a time
     constexpr int BJ = BN / 32, BI = BM / 16;
-    const int gq = lane >> 4, jx = lane & 15;
+    const int gq = elane >> 4, jx = elane & 15;
 #pragma unroll 4
     for (int b = wave; b < BJ * BI; b += NW) {
       const int jb = (b % BJ) * 32, ib = (b / BJ) * 16;
@@ -545,6 +564,10 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), dr, off, 0, 0);
     }
   }
+  // the next tile's loads overwrite the staging area: every wave must have
+  // read its part first (the stores themselves may still be in flight)
+  __syncthreads();
+  }
 }
 
 template <int T, bool TM, bool TN, int EPI>
@@ -553,9 +576,12 @@ hipError_t go(hipStream_t s, const NsGemmArgs& a) {
   // of 64 x 64.  BK = 64, two stage buffers.
   constexpr int NWN = T == 256 ? 4 : 2;
   constexpr int BK = 64, NS = 2;
-  const int64_t grid = a.units * a.tiles_per_unit;
-  if (grid <= 0) return hipSuccess;
-  if (grid > 0x7fffffffLL / 512) return hipErrorInvalidValue;
+  const int64_t tiles = a.units * a.tiles_per_unit;
+  if (tiles <= 0) return hipSuccess;
+  // one workgroup per CU for 256-tiles (LDS and registers of a CU), two for
+  // 128-tiles; each walks its tiles in turn
+  const int64_t cap = static_cast<int64_t>(a.cus > 0 ? a.cus : 256) * (T == 256 ? 1 : 2);
+  const int64_t grid = tiles < cap ? tiles : cap;
   ns_gemm_mfma_kernel<T, T, NWN, BK, NS, TM, TN, EPI><<<static_cast<unsigned>(grid), 128 * NWN, 0, s>>>(a);
   return hipGetLastError();
 }

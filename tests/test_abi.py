@@ -53,11 +53,23 @@ def test_create_without_gpu_fails_cleanly():
     assert lib.muon_destroy(None) == _lib.MUON_OK
 
 
+def test_struct_and_enum_mirrors_match_header():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} muon_ns_params_t;", text).group(1)
+    fields = re.findall(r"([a-z_]+)(?:\s*,\s*([a-z_]+))?(?:\s*,\s*([a-z_]+))?\s*;", body)
+    names = [n for grp in fields for n in grp if n]
+    assert names == [f for f, _ in _lib.NsParams._fields_]
+    count = int(re.search(r"MUON_K_COUNT\s*=\s*(\d+)", text).group(1))
+    assert len(_lib.KERNEL_CLASSES) == count
+    assert int(re.search(r"MUON_NS_GRAM\s*=\s*(\d+)", text).group(1)) == 1
+
+
 def test_null_context_rejected():
     lib = _lib.load()
     p = _lib.NsParams()
     lib.muon_ns_params_default(ctypes.byref(p))
     assert (p.steps, round(p.a, 4), round(p.b, 4), round(p.c, 4), p.compute) == (5, 3.4445, -4.775, 2.0315, 1)
+    assert p.method == 0
     assert lib.muon_momentum_update(None, None, None, 1, None, None, 1, 10, 0.95, 1) == _lib.MUON_EINVAL
     assert lib.muon_apply(None, None, None, None, 1, None, 10, 0.02, 1.0, 0.0) == _lib.MUON_EINVAL
     assert lib.muon_newton_schulz_batched(None, None, None, 1, _lib.Shape(8, 8, 0), 1, ctypes.byref(p),
