@@ -10,7 +10,9 @@ fp32 momentum pre-filled by two momentum steps, fp32 masters ~ N(0, 0.02)).
 Prints ONE JSON line.  `value` is Newton-Schulz algorithmic TFLOP per step
 divided by the whole step's wall time; ms_per_step is the full step.  Per-
 kernel durations come from HIP events the library records on the launch
-stream around every kernel during the timed steps.
+stream around every kernel during the timed steps.  --ns-method gram runs
+the Gram form instead; `value` then still counts the quintic's flops
+(quintic-equivalent throughput) and the breakdown the executed ones.
 """
 from __future__ import annotations
 
@@ -36,6 +38,21 @@ def ns_flops(m: int, n: int, steps: int = 5):
     symsq = m * m * (m + 1)
     upd = 2 * m * m * n
     return steps * gram, steps * symsq, steps * upd
+
+
+def ns_flops_gram(m: int, n: int, steps: int = 5):
+    """Algorithmic flops of one unit in the Gram form: A_0 = X X^T (symmetric,
+    m(m+1)n), steps symmetric squares P_k, 3 (steps - 1) symmetric m x m
+    products (Q_{k+1} = P_k Q_k, P_k A_k, (P_k A_k) P_k), one final 2 m^2 n."""
+    if steps == 0:
+        return 0, 0, 0, 0
+    sq = m * m * (m + 1)
+    return m * (m + 1) * n, steps * sq, 3 * (steps - 1) * sq, 2 * m * m * n
+
+
+def uses_gram_form(m: int, n: int, compute: str) -> bool:
+    """bf16 runs the Gram form on units with 2 m <= n (the library's rule)."""
+    return compute == "f32" or 2 * m <= n
 
 
 def workload_by_name(name):
@@ -140,6 +157,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_4b")
+    ap.add_argument("--ns-method", default="quintic", choices=["quintic", "gram"],
+                    help="Newton-Schulz evaluation; value stays the quintic's flops / step time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip per-kernel event timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -165,10 +184,10 @@ def main():
         return
     w = workload_by_name(args.workload)
     shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
-    keep_bf16 = args.workload != "qwen3_30b_experts"
+    keep_bf16 = not args.workload.startswith("qwen3_30b_experts")
     ms = MuonStep(shapes, dev, lr=w.lr, beta=w.beta, nesterov=w.nesterov, compute=w.compute,
                   grad_dtype=w.grad_dtype, cap_bytes=w.cap_bytes, cap_kind=w.cap_kind,
-                  ns_steps=w.ns_steps, keep_bf16_weights=keep_bf16)
+                  ns_steps=w.ns_steps, keep_bf16_weights=keep_bf16, ns_method=args.ns_method)
     g = torch.Generator(device=dev).manual_seed(w.seed)
     for i, W0 in enumerate(synth.draw_weights(w, g, dev)):
         ms.view(ms.master, i).copy_(W0)
@@ -206,7 +225,20 @@ def main():
     f_upd = sum(f[2] for f in fl)
     f_ns = f_gram + f_symsq + f_upd
     dense = sum(w.ns_steps * (2 * m * m * n + 2 * m ** 3 + 2 * m * m * n) for (m, n) in units)
+    # `value` counts the quintic iteration's algorithmic flops in both modes
+    # (for the Gram form: quintic-equivalent throughput); the per-class rates
+    # use the flops each class actually executed
     value = f_ns / (ms_per_step * 1e-3) / 1e12
+    ex = {"gram": 0, "symsq": 0, "prod": 0, "update": 0}
+    for (m, n) in units:
+        if args.ns_method == "gram" and uses_gram_form(m, n, w.compute):
+            fg, fs, fp, fu = ns_flops_gram(m, n, w.ns_steps)
+        else:
+            (fg, fs, fu), fp = ns_flops(m, n, w.ns_steps), 0
+        ex["gram"] += fg
+        ex["symsq"] += fs
+        ex["prod"] += fp
+        ex["update"] += fu
     numel = sum(m.numel for m in w.mats)
     gdt_b = 2 if w.grad_dtype == torch.bfloat16 else 4
     cdt_b = 2 if w.compute == "bf16" else 4
@@ -222,17 +254,20 @@ def main():
         def tf(f, k):
             t = per_step[k][0]
             return round(f / (t * 1e-3) / 1e12, 2) if t > 0 else None
-        breakdown["gram"]["tflops"] = tf(f_gram, "gram")
-        breakdown["symsq"]["tflops"] = tf(f_symsq, "symsq")
-        breakdown["update"]["tflops"] = tf(f_upd, "update")
-        ns_ms = sum(per_step[k][0] for k in ("norm", "gram", "symsq", "update"))
+        for k in ("gram", "symsq", "prod", "update"):
+            if per_step[k][1] > 0:
+                breakdown[k]["tflops"] = tf(ex[k], k)
+        if per_step["prod"][1] == 0:
+            del breakdown["prod"]
+        ns_ms = sum(per_step[k][0] for k in ("norm", "gram", "symsq", "prod", "update"))
         breakdown["newton_schulz"] = {"ms_per_step": round(ns_ms, 4),
-                                      "tflops": round(f_ns / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None}
+                                      "tflops": round(sum(ex.values()) / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None}
         for k, b in (("momentum", mom_bytes), ("apply", app_bytes)):
             t = per_step[k][0]
             breakdown[k]["gbs"] = round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
             breakdown[k]["frac_hbm"] = round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if t > 0 else None
         t_upd, n_upd = per_step["update"]
+        f_upd = ex["update"]
         if n_upd > 0 and t_upd > 0:
             achieved = f_upd / (t_upd * 1e-3) / 1e12
             traffic = traffic_record(os.path.join(ROOT, "newton_schulz_amd", "csrc", "ns_gemm_mfma.hip"))
@@ -243,7 +278,8 @@ def main():
                         "flop_per_launch_avg": int(f_upd / n_upd)}
 
     out = {
-        "metric": METRIC,
+        "metric": METRIC if args.ns_method == "quintic" else METRIC.replace(
+            "Newton–Schulz TFLOP/s", "Newton–Schulz quintic-equivalent TFLOP/s, gram form"),
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -256,13 +292,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1e-3) bf16 gradients, fp32 state; no checkpoint)",
         "config": {"workload": w.name, "matrices": len(w.mats), "muon_params": numel,
-                   "ns_units": len(units), "ns_steps": w.ns_steps,
+                   "ns_units": len(units), "ns_steps": w.ns_steps, "ns_method": args.ns_method,
                    "micro_bucket_cap_bytes": w.cap_bytes, "cap_kind": w.cap_kind,
                    "micro_buckets": len(ms.plan.buckets), "workspace_bytes": ms.plan.max_workspace,
                    "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "ns_tflop_per_step_algorithmic": round(f_ns / 1e12, 4),
         "ns_tflop_per_step_dense_equiv": round(dense / 1e12, 4),
+        "ns_tflop_per_step_executed": round(sum(ex.values()) / 1e12, 4),
         "matrices_per_s": round(len(units) / (ms_per_step * 1e-3), 1),
         "wall_s_timed": round(wall, 3),
         "breakdown": breakdown,
