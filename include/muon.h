@@ -152,10 +152,17 @@ typedef struct {
  * matrices whose cost stays within `cap_bytes` (blog sections "Chunked
  * communication" and "Memory control", item 1: a separate Muon cap;
  * estimate_muon_peak(bucket) <= cap).  A matrix larger than the cap gets a
- * micro-bucket of its own, flagged over_cap.  Host only; *out is owned by
- * the caller (muon_plan_destroy).  Errors: MUON_EINVAL, MUON_ESHAPE. */
+ * micro-bucket of its own, flagged over_cap.
+ * compute_units = 0: micro-buckets are filled greedily up to the cap.
+ * compute_units = C > 0 (the device's CU count): the cut points are chosen,
+ * still under the cap, to minimise a model of the Newton-Schulz time on C
+ * CUs -- each product launch takes ceil(tiles / C) rounds of its per-tile
+ * k-length -- plus a fixed cost per micro-bucket, so that launches do not end
+ * with a nearly empty last round of tiles.  Host only; *out is owned by the
+ * caller (muon_plan_destroy).  Errors: MUON_EINVAL, MUON_ESHAPE. */
 muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t count, size_t cap_bytes,
-                               int32_t cap_kind, int32_t compute, muon_plan_t** out);
+                               int32_t cap_kind, int32_t compute, int32_t compute_units,
+                               muon_plan_t** out);
 int64_t muon_plan_num_buckets(const muon_plan_t* plan);
 /* Info on micro-bucket `b`; when `indices` is non-NULL it receives info->count
  * matrix indices (positions in the `shapes` array), in execution order. */

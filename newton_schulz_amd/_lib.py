@@ -60,7 +60,7 @@ def load() -> ctypes.CDLL:
         "muon_ctx_workspace_bytes": (sz, [vp]),
         "muon_ns_params_default": (None, [P(NsParams)]),
         "muon_ns_workspace_bytes": (sz, [Shape, i64, i32]),
-        "muon_plan_create": (i32, [P(Shape), i64, sz, i32, i32, P(vp)]),
+        "muon_plan_create": (i32, [P(Shape), i64, sz, i32, i32, i32, P(vp)]),
         "muon_plan_num_buckets": (i64, [vp]),
         "muon_plan_bucket": (i32, [vp, i64, P(BucketInfo), P(i64)]),
         "muon_plan_max_workspace": (sz, [vp]),

@@ -203,13 +203,14 @@ class Plan:
     """Host scheduler result: micro-buckets of whole matrices under a cap."""
 
     def __init__(self, shapes: Sequence[Tuple[int, int, int]], cap_bytes: int, cap_kind: str = "full",
-                 compute: str = "bf16"):
+                 compute: str = "bf16", compute_units: int = 0):
         lib = _lib.load()
         arr = (Shape * len(shapes))(*[Shape(r, c, h) for (r, c, h) in shapes])
         h = ctypes.c_void_p()
         kind = MUON_CAP_FULL_BYTES if cap_kind == "full" else MUON_CAP_WORKSPACE
         st = lib.muon_plan_create(arr, len(shapes), int(cap_bytes), kind,
-                                  MUON_BF16 if compute == "bf16" else MUON_F32, ctypes.byref(h))
+                                  MUON_BF16 if compute == "bf16" else MUON_F32, int(compute_units),
+                                  ctypes.byref(h))
         if st != _lib.MUON_OK:
             raise MuonError(st, "muon_plan_create")
         try:

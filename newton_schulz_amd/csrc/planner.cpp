@@ -20,6 +20,29 @@ namespace {
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Model of the Newton-Schulz time of one micro-bucket of U units of
+// canonical shape (m, n) on `cus` compute units, in k-elements processed per
+// tile slot: every product launch takes ceil(tiles / slots) rounds, a round
+// as long as its contraction (Gram: n, symmetric square and update: m).
+// Tile side and slots per CU follow the kernels: 256 x 256 (one per CU) once
+// m >= 256 in bf16, else 128 x 128 (two per CU); fp32 runs 64 x 64 tiles.
+double ns_time_model(int64_t m, int64_t n, int64_t units, int cus, int32_t compute) {
+  const int64_t tile = compute == MUON_F32 ? 64 : (m >= 256 ? 256 : 128);
+  const int64_t slots = static_cast<int64_t>(cus) * (tile == 256 ? 1 : (tile == 128 ? 2 : 4));
+  const int64_t tm = ceil_div(m, tile), tn = ceil_div(n, tile);
+  const int64_t rounds_sym = ceil_div(units * (tm * (tm + 1) / 2), slots);
+  const int64_t rounds_upd = ceil_div(units * tm * tn, slots);
+  return static_cast<double>(rounds_sym) * static_cast<double>(n + m) +
+         static_cast<double>(rounds_upd) * static_cast<double>(m);
+}
+
+// Fixed cost of one more micro-bucket in the same units: about 20 dependent
+// launches (momentum, norm, the products, apply) at a few microseconds each,
+// with ~19 ns per k-element of a 256-wide tile round.
+constexpr double kBucketOverhead = 3000.0;
+
 }  // namespace
 
 // Shared with muon_api.hip, so the reported size and the carve-up agree.
@@ -83,7 +106,7 @@ static bool same_shape(const muon_shape_t& x, const muon_shape_t& y) {
 
 extern "C" muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t count,
                                           size_t cap_bytes, int32_t cap_kind, int32_t compute,
-                                          muon_plan_t** out) {
+                                          int32_t compute_units, muon_plan_t** out) {
   if (out == nullptr || (count > 0 && shapes == nullptr) || count < 0) return MUON_EINVAL;
   if (cap_kind != MUON_CAP_FULL_BYTES && cap_kind != MUON_CAP_WORKSPACE) return MUON_EINVAL;
   if (compute != MUON_BF16 && compute != MUON_F32) return MUON_EDTYPE;
@@ -165,13 +188,58 @@ extern "C" muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t co
         cur.clear();
         cur_cost = 0;
       };
-      for (int64_t i : sorted) {
-        const size_t c = cost(i);
-        if (!cur.empty() && cur_cost + c > cap_bytes) flush();
-        cur.push_back(i);
-        cur_cost += c;
+      if (compute_units <= 0) {
+        for (int64_t i : sorted) {
+          const size_t c = cost(i);
+          if (!cur.empty() && cur_cost + c > cap_bytes) flush();
+          cur.push_back(i);
+          cur_cost += c;
+        }
+        flush();
+      } else {
+        // cut points minimising the time model: best[i] = cheapest plan of
+        // the first i members, each micro-bucket a run within the cap (or a
+        // single matrix)
+        const size_t N = sorted.size();
+        std::vector<size_t> c(N);
+        std::vector<int64_t> u(N);
+        for (size_t i = 0; i < N; ++i) {
+          const muon_shape_t& sh = shapes[sorted[i]];
+          c[i] = cost(sorted[i]);
+          u[i] = sh.head_rows > 0 ? sh.rows / sh.head_rows : 1;
+        }
+        std::vector<double> best(N + 1, 0.0);
+        std::vector<size_t> from(N + 1, 0);
+        for (size_t i = 1; i <= N; ++i) {
+          best[i] = -1.0;
+          size_t bytes = 0;
+          int64_t units = 0;
+          for (size_t j = i; j-- > 0;) {
+            bytes += c[j];
+            units += u[j];
+            if (j + 1 < i && bytes > cap_bytes) break;
+            const double t = best[j] + kBucketOverhead +
+                             ns_time_model(keys[b].first, keys[b].second, units, compute_units,
+                                           compute);
+            if (best[i] < 0.0 || t < best[i]) {
+              best[i] = t;
+              from[i] = j;
+            }
+          }
+        }
+        std::vector<size_t> cuts;
+        for (size_t i = N; i > 0; i = from[i]) cuts.push_back(i);
+        std::reverse(cuts.begin(), cuts.end());
+        size_t start = 0;
+        for (size_t end : cuts) {
+          for (size_t q = start; q < end; ++q) {
+            cur.push_back(sorted[q]);
+            cur_cost += c[q];
+          }
+          flush();
+          start = end;
+        }
       }
-      flush();
     }
   } catch (...) {
     delete plan;

@@ -35,7 +35,8 @@ class MuonStep:
         self.compute = compute
         self.cdtype = torch.bfloat16 if compute == "bf16" else torch.float32
         self.params = ns_params(steps=ns_steps, compute=compute, method=ns_method)
-        self.plan = Plan(self.shapes, cap_bytes, cap_kind, compute)
+        cus = torch.cuda.get_device_properties(self.device).multi_processor_count
+        self.plan = Plan(self.shapes, cap_bytes, cap_kind, compute, compute_units=cus)
 
         # flat layout: matrices in plan order
         self.order: List[int] = [i for b in self.plan.buckets for i in b.indices]

@@ -134,6 +134,38 @@ def test_plan_qwen3_4b_buckets():
     assert plan.max_workspace == max(b.workspace_bytes for b in plan.buckets)
 
 
+def _round_cost(m, n, units, cus=256):
+    # k-elements per tile slot of one bucket's product launches, rounds of
+    # ceil(tiles / CUs) (256 x 256 tiles, one per CU)
+    t, tn = -(-m // 256), -(-n // 256)
+    sym = -(-(units * t * (t + 1) // 2) // cus)
+    upd = -(-(units * t * tn) // cus)
+    return sym * (n + m) + upd * m
+
+
+def test_plan_wave_aware_cuts_qwen3_4b():
+    w = synth.qwen3_4b(layers=36)
+    shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
+    plan = Plan(shapes, 512 << 20, "full", "bf16", compute_units=256)
+    flat = [i for b in plan.buckets for i in b.indices]
+    assert sorted(flat) == list(range(len(shapes)))
+    for b in plan.buckets:
+        assert b.full_bytes <= 512 << 20 and not b.over_cap
+    counts = {}
+    for b in plan.buckets:
+        counts.setdefault((b.m, b.n), []).append(b.count)
+    # (2560, 9728): 10 per micro-bucket (cap-filling) leaves 550 Gram tiles =
+    # 2.15 rounds on 256 CUs, so 9 (495 tiles, 2 rounds) is cheaper per matrix
+    assert counts[(2560, 9728)] == [9] * 12
+    assert _round_cost(2560, 9728, 9) / 9 < _round_cost(2560, 9728, 10) / 10
+    assert sum(counts[(2560, 4096)]) == 72 and max(counts[(2560, 4096)]) <= 25
+    assert counts[(1024, 2560)] == [72]
+    # the cut plan never models slower than the greedy one
+    greedy = Plan(shapes, 512 << 20, "full", "bf16")
+    cost = lambda p: sum(_round_cost(b.m, b.n, b.units) for b in p.buckets)
+    assert cost(plan) < cost(greedy)
+
+
 def test_plan_workspace_cap_experts():
     w = synth.qwen3_30b_experts(layers=2)
     shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
