@@ -541,7 +541,9 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
       val = __builtin_bit_cast(u32x4_t, h);
     }
     const uint32_t off = (i < a.M && j < a.N) ? static_cast<uint32_t>(i * ldd + j) * 2u : kOOB;
-    __builtin_amdgcn_raw_buffer_store_b128(val, dr, off, 0, 0);
+    // the update's output is read back only by the next launch, after far
+    // more traffic than the caches hold: store it non-temporally (nt)
+    __builtin_amdgcn_raw_buffer_store_b128(val, dr, off, 0, EPI == EPI_UPDATE ? 2 : 0);
   }
   if (EPI != EPI_UPDATE && !diag) {
     // mirror: row j of the output gets C[i .. i + 7][j] from two transposed
