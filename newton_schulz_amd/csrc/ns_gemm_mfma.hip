@@ -286,19 +286,24 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   const int wm = wave / NWN, wn = wave % NWN;
 
   // Persistent tiles: workgroup hw runs on XCD hw % 8 (round-robin dispatch,
-  // each XCD with its own L2).  XCD x owns one contiguous run of tiles,
-  // shared among its cnt workgroups in strides of cnt, so at any moment the
-  // workgroups of an XCD work on neighbouring tiles.  A workgroup moves on to
-  // its next tile without leaving the CU: the loads of the next tile start
-  // while the stores of the last one drain.
+  // each XCD with its own L2), and the cnt workgroups of an XCD always work on
+  // cnt neighbouring tiles, which share operand panels in L2.  Gram and
+  // update hand out those chunks of cnt tiles round-robin over the XCDs, so
+  // all XCDs work on the same few units at once and share their panels in
+  // the MALL (1-3% faster there); the symmetric square keeps one contiguous
+  // run per XCD (the round-robin order measured 2% slower for it).  A
+  // workgroup moves on to its next tile without leaving the CU.
   const int64_t total = a.units * a.tiles_per_unit;
   const int G = static_cast<int>(gridDim.x), hw = static_cast<int>(blockIdx.x);
   const int xg = hw % 8, q8 = G / 8, r8 = G % 8;
   const int cnt = q8 + (xg < r8 ? 1 : 0);
+  const bool rr = EPI != EPI_SYMSQ && r8 == 0;
   const int64_t P = static_cast<int64_t>(xg) * q8 + min(xg, r8);
-  const int64_t t_end = total * (P + cnt) / G;
+  const int64_t t_first = rr ? static_cast<int64_t>(xg) * q8 + hw / 8 : total * P / G + hw / 8;
+  const int64_t t_end = rr ? total : total * (P + cnt) / G;
+  const int64_t t_step = rr ? G : cnt;
 
-  for (int64_t lid = total * P / G + hw / 8; lid < t_end; lid += cnt) {
+  for (int64_t lid = t_first; lid < t_end; lid += t_step) {
   const int64_t u = lid / a.tiles_per_unit;
   const int t = static_cast<int>(lid - u * a.tiles_per_unit);
   int ti, tj;
