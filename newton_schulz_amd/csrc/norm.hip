@@ -27,27 +27,47 @@ __global__ __launch_bounds__(256) void norm_partial_kernel(NsNormArgs a) {
   if (VEC) {
     // start is a multiple of 8; full 8-element groups first
     const int64_t nfull = (end > start) ? (end - start) / 8 : 0;
-    for (int64_t g = threadIdx.x; g < nfull; g += 256) {
-      const int64_t e = start + 8 * g;
+    // four groups per trip, all loaded before the first use (more bytes in
+    // flight per thread); a group past the chunk contributes zeros
+    constexpr int U = 4;
+    for (int64_t g0 = threadIdx.x; g0 < nfull; g0 += 256 * U) {
       if (sizeof(T) == 2) {
-        const uint4 v = *reinterpret_cast<const uint4*>(base + e);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        double d = 0.0;
+        uint4 v[U];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
-          d += static_cast<double>(lo * lo);
-          d += static_cast<double>(hi * hi);
+        for (int r = 0; r < U; ++r) {
+          const int64_t g = g0 + 256 * r;
+          v[r] = g < nfull ? *reinterpret_cast<const uint4*>(base + start + 8 * g)
+                           : make_uint4(0, 0, 0, 0);
         }
-        acc += d;
-      } else {
-        const float4* q = reinterpret_cast<const float4*>(base + e);
-        const float4 x = q[0], y = q[1];
-        const float v[8] = {x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w};
-        double d = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) d += static_cast<double>(v[i]) * static_cast<double>(v[i]);
-        acc += d;
+        for (int r = 0; r < U; ++r) {
+          const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
+          double d = 0.0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
+            d += static_cast<double>(lo * lo);
+            d += static_cast<double>(hi * hi);
+          }
+          acc += d;
+        }
+      } else {
+        float4 x[U], y[U];
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+          const int64_t g = g0 + 256 * r;
+          const float4* q = reinterpret_cast<const float4*>(base + start + 8 * g);
+          x[r] = g < nfull ? q[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+          y[r] = g < nfull ? q[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int r = 0; r < U; ++r) {
+          const float v[8] = {x[r].x, x[r].y, x[r].z, x[r].w, y[r].x, y[r].y, y[r].z, y[r].w};
+          double d = 0.0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) d += static_cast<double>(v[i]) * static_cast<double>(v[i]);
+          acc += d;
+        }
       }
     }
     for (int64_t e = start + 8 * nfull + threadIdx.x; e < end; e += 256) {
