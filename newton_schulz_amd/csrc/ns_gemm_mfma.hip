@@ -32,8 +32,11 @@
 // stages (the loads of stage k+1 fly while stage k feeds the MFMAs).  The
 // epilogue stages the bf16 tile through LDS so global stores are 16-byte and
 // row-contiguous, and writes the mirror tile of symmetric outputs from
-// transposed LDS reads.  Workgroup ids are remapped so each XCD (own L2)
-// gets a contiguous run of tiles.
+// transposed LDS reads.  The grid is persistent (one workgroup per CU, each
+// walking its tiles); the workgroups of one XCD (own L2) always work on
+// neighbouring tiles.  The same kernel also serves the m x m products of the
+// Gram form of the iteration (P Q for symmetric commuting P, Q through the
+// Gram epilogue).
 #include "muon_device.h"
 #include "muon_internal.h"
 
