@@ -17,7 +17,6 @@ the Gram form instead; `value` then still counts the quintic's flops
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -86,9 +85,9 @@ def traffic_record(kernel_src: str):
     path = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_4b.json")
     if not os.path.exists(path):
         return None
+    from newton_schulz_amd.prof import source_fingerprint
     rec = json.load(open(path))
-    h = hashlib.sha256(open(kernel_src, "rb").read()).hexdigest()[:16]
-    if rec.get("source_sha256_16") != h:
+    if rec.get("source_code_sha256_16") != source_fingerprint(kernel_src):
         return None
     return round(rec.get("hbm_bytes_per_launch"))
 
