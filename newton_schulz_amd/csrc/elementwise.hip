@@ -1,10 +1,15 @@
 // Streaming kernels of the Muon step: momentum (+ Nesterov) and weight apply.
 //
-// Both are HBM-bound passes; each thread moves 8 elements per iteration with
-// 16-byte (bf16) / 32-byte (fp32) vector accesses, grid-stride over the flat
-// range.  Every arithmetic operation is a separate IEEE binary32 operation
-// rounded to nearest-even (contraction is disabled for this file), so the
-// results are bit-identical to a binary32 evaluation of the same sequence.
+// Both are HBM-bound passes.  The vector path is a one-shot launch: workgroup
+// b owns the 4096 consecutive elements [4096 b, 4096 b + 4096), each thread
+// two groups of 8 elements 2048 apart, all loads issued before any store, with
+// 16-byte (bf16) / 32-byte (fp32) accesses.  On MI355X this streams ~10%
+// faster than a persistent grid-stride loop over the same range: the
+// dispatcher hands out workgroups in address order, so the HBM pages in use
+// at any moment stay few.  Unaligned ranges take a grid-stride scalar loop.
+// Every arithmetic operation is a separate IEEE binary32 operation rounded to
+// nearest-even (contraction is disabled for this file), so the results are
+// bit-identical to a binary32 evaluation of the same sequence.
 #include "muon_device.h"
 #include "muon_internal.h"
 
@@ -14,6 +19,9 @@ using muon::bf16_t;
 
 namespace {
 
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+
 template <typename T> struct Vec8;
 template <> struct Vec8<float> {
   float v[8];
@@ -22,10 +30,17 @@ template <> struct Vec8<float> {
     float4 a = q[0], b = q[1];
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
+  template <bool NT = false>
   __device__ __forceinline__ void store(float* p) const {
-    float4* q = reinterpret_cast<float4*>(p);
-    q[0] = make_float4(v[0], v[1], v[2], v[3]);
-    q[1] = make_float4(v[4], v[5], v[6], v[7]);
+    f32x4_nt* q = reinterpret_cast<f32x4_nt*>(p);
+    const f32x4_nt a = {v[0], v[1], v[2], v[3]}, b = {v[4], v[5], v[6], v[7]};
+    if (NT) {
+      __builtin_nontemporal_store(a, q);
+      __builtin_nontemporal_store(b, q + 1);
+    } else {
+      q[0] = a;
+      q[1] = b;
+    }
   }
 };
 template <> struct Vec8<bf16_t> {
@@ -39,13 +54,17 @@ template <> struct Vec8<bf16_t> {
       v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
     }
   }
+  template <bool NT = false>
   __device__ __forceinline__ void store(bf16_t* p) const {
     uint4 a;
     a.x = muon::pack_bf16x2(v[0], v[1]);
     a.y = muon::pack_bf16x2(v[2], v[3]);
     a.z = muon::pack_bf16x2(v[4], v[5]);
     a.w = muon::pack_bf16x2(v[6], v[7]);
-    *reinterpret_cast<uint4*>(p) = a;
+    if (NT)
+      __builtin_nontemporal_store(u32x4_nt{a.x, a.y, a.z, a.w}, reinterpret_cast<u32x4_nt*>(p));
+    else
+      *reinterpret_cast<uint4*>(p) = a;
   }
 };
 
@@ -63,40 +82,63 @@ __device__ __forceinline__ void momentum_one(float g, float& m, float& u, float 
   }
 }
 
-template <typename G, typename U, bool VEC>
-__global__ __launch_bounds__(256) void momentum_kernel(const G* __restrict__ grad,
-                                                       float* __restrict__ mom,
-                                                       U* __restrict__ upd, int64_t numel,
-                                                       float beta, float c1, int nesterov) {
+// one-shot vector path: EW_U groups of 8 elements per thread, EW_BS threads
+constexpr int EW_BS = 256, EW_U = 2;
+constexpr int64_t EW_BLOCK = 8 * EW_U * EW_BS;  // elements per workgroup
+
+template <typename G, typename U>
+__global__ __launch_bounds__(EW_BS) void momentum_vec_kernel(const G* __restrict__ grad,
+                                                             float* __restrict__ mom,
+                                                             U* __restrict__ upd, int64_t numel,
+                                                             float beta, float c1, int nesterov) {
+  const bool nes = nesterov != 0;
+  const int64_t nvec = numel / 8;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * (EW_U * EW_BS) + threadIdx.x;
+  Vec8<G> g[EW_U];
+  Vec8<float> m[EW_U];
+#pragma unroll
+  for (int k = 0; k < EW_U; ++k) {
+    const int64_t i = base + k * EW_BS;
+    if (i < nvec) {
+      g[k].load(grad + 8 * i);
+      m[k].load(mom + 8 * i);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < EW_U; ++k) {
+    const int64_t i = base + k * EW_BS;
+    if (i < nvec) {
+      Vec8<U> u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) momentum_one(g[k].v[e], m[k].v[e], u.v[e], beta, c1, nes);
+      // the momentum is next read a whole step later: do not keep it cached
+      m[k].template store<true>(mom + 8 * i);
+      u.store(upd + 8 * i);
+    }
+  }
+  if (blockIdx.x == gridDim.x - 1) {  // the last numel % 8 elements
+    for (int64_t i = nvec * 8 + threadIdx.x; i < numel; i += EW_BS) {
+      float mm = mom[i], u;
+      momentum_one(muon::Elem<G>::load(grad + i), mm, u, beta, c1, nes);
+      mom[i] = mm;
+      muon::Elem<U>::store(upd + i, u);
+    }
+  }
+}
+
+template <typename G, typename U>
+__global__ __launch_bounds__(256) void momentum_scalar_kernel(const G* __restrict__ grad,
+                                                              float* __restrict__ mom,
+                                                              U* __restrict__ upd, int64_t numel,
+                                                              float beta, float c1, int nesterov) {
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t nth = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const bool nes = nesterov != 0;
-  if (VEC) {
-    const int64_t nvec = numel / 8;
-    for (int64_t i = tid; i < nvec; i += nth) {
-      Vec8<G> g;
-      Vec8<float> m;
-      Vec8<U> u;
-      g.load(grad + 8 * i);
-      m.load(mom + 8 * i);
-#pragma unroll
-      for (int k = 0; k < 8; ++k) momentum_one(g.v[k], m.v[k], u.v[k], beta, c1, nes);
-      m.store(mom + 8 * i);
-      u.store(upd + 8 * i);
-    }
-    for (int64_t i = nvec * 8 + tid; i < numel; i += nth) {
-      float m = mom[i], u;
-      momentum_one(muon::Elem<G>::load(grad + i), m, u, beta, c1, nes);
-      mom[i] = m;
-      muon::Elem<U>::store(upd + i, u);
-    }
-  } else {
-    for (int64_t i = tid; i < numel; i += nth) {
-      float m = mom[i], u;
-      momentum_one(muon::Elem<G>::load(grad + i), m, u, beta, c1, nes);
-      mom[i] = m;
-      muon::Elem<U>::store(upd + i, u);
-    }
+  for (int64_t i = tid; i < numel; i += nth) {
+    float m = mom[i], u;
+    momentum_one(muon::Elem<G>::load(grad + i), m, u, beta, c1, nes);
+    mom[i] = m;
+    muon::Elem<U>::store(upd + i, u);
   }
 }
 
@@ -106,43 +148,72 @@ __device__ __forceinline__ float apply_one(float w, float u, float eta, float de
   return w1 - step;
 }
 
-template <typename U, bool VEC, bool WANT_BF16>
-__global__ __launch_bounds__(256) void apply_kernel(float* __restrict__ master,
-                                                    const U* __restrict__ upd,
-                                                    bf16_t* __restrict__ wbf, int64_t numel,
-                                                    float eta, float decay, int has_wd) {
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t nth = static_cast<int64_t>(gridDim.x) * blockDim.x;
+template <typename U, bool WANT_BF16>
+__global__ __launch_bounds__(EW_BS) void apply_vec_kernel(float* __restrict__ master,
+                                                          const U* __restrict__ upd,
+                                                          bf16_t* __restrict__ wbf, int64_t numel,
+                                                          float eta, float decay, int has_wd) {
   const bool wd = has_wd != 0;
-  int64_t start_tail = 0;
-  if (VEC) {
-    const int64_t nvec = numel / 8;
-    for (int64_t i = tid; i < nvec; i += nth) {
-      Vec8<float> w;
-      Vec8<U> u;
-      w.load(master + 8 * i);
-      u.load(upd + 8 * i);
+  const int64_t nvec = numel / 8;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * (EW_U * EW_BS) + threadIdx.x;
+  Vec8<float> w[EW_U];
+  Vec8<U> u[EW_U];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) w.v[k] = apply_one(w.v[k], u.v[k], eta, decay, wd);
-      w.store(master + 8 * i);
+  for (int k = 0; k < EW_U; ++k) {
+    const int64_t i = base + k * EW_BS;
+    if (i < nvec) {
+      w[k].load(master + 8 * i);
+      u[k].load(upd + 8 * i);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < EW_U; ++k) {
+    const int64_t i = base + k * EW_BS;
+    if (i < nvec) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) w[k].v[e] = apply_one(w[k].v[e], u[k].v[e], eta, decay, wd);
+      // neither copy of the weights is read again within the step
+      w[k].template store<true>(master + 8 * i);
       if (WANT_BF16) {
         Vec8<bf16_t> b;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) b.v[k] = w.v[k];
-        b.store(wbf + 8 * i);
+        for (int e = 0; e < 8; ++e) b.v[e] = w[k].v[e];
+        b.template store<true>(wbf + 8 * i);
       }
     }
-    start_tail = nvec * 8;
   }
-  for (int64_t i = start_tail + tid; i < numel; i += nth) {
-    const float w = apply_one(master[i], muon::Elem<U>::load(upd + i), eta, decay, wd);
-    master[i] = w;
-    if (WANT_BF16) wbf[i] = muon::f32_to_bf16(w);
+  if (blockIdx.x == gridDim.x - 1) {  // the last numel % 8 elements
+    for (int64_t i = nvec * 8 + threadIdx.x; i < numel; i += EW_BS) {
+      const float x = apply_one(master[i], muon::Elem<U>::load(upd + i), eta, decay, wd);
+      master[i] = x;
+      if (WANT_BF16) wbf[i] = muon::f32_to_bf16(x);
+    }
   }
 }
 
+template <typename U, bool WANT_BF16>
+__global__ __launch_bounds__(256) void apply_scalar_kernel(float* __restrict__ master,
+                                                           const U* __restrict__ upd,
+                                                           bf16_t* __restrict__ wbf, int64_t numel,
+                                                           float eta, float decay, int has_wd) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nth = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const bool wd = has_wd != 0;
+  for (int64_t i = tid; i < numel; i += nth) {
+    const float x = apply_one(master[i], muon::Elem<U>::load(upd + i), eta, decay, wd);
+    master[i] = x;
+    if (WANT_BF16) wbf[i] = muon::f32_to_bf16(x);
+  }
+}
+
+// one workgroup per EW_BLOCK elements (at least one, for the scalar tail)
+inline unsigned vec_grid(int64_t numel) {
+  const int64_t blocks = (numel / 8 + EW_U * EW_BS - 1) / (EW_U * EW_BS);
+  return static_cast<unsigned>(blocks < 1 ? 1 : blocks);
+}
+
 inline unsigned stream_grid(int64_t work_items, int cus) {
-  // enough waves to saturate HBM: up to 8 workgroups of 256 threads per CU
+  // grid-stride scalar path: up to 8 workgroups of 256 threads per CU
   int64_t blocks = (work_items + 255) / 256;
   const int64_t cap = static_cast<int64_t>(cus) * 8;
   if (blocks > cap) blocks = cap;
@@ -157,18 +228,17 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 hipError_t launch_momentum(hipStream_t s, int cus, const void* grad, int gdt, float* mom,
                            void* upd, int udt, int64_t numel, float beta, float c1,
                            int nesterov) {
+  if (numel <= 0) return hipSuccess;
+  if (numel / 8 >= (int64_t{1} << 40)) return hipErrorInvalidValue;  // beyond a 1-D grid
   const bool vec = aligned(grad, 16) && aligned(mom, 16) && aligned(upd, 16);
-  const unsigned grid = stream_grid(vec ? (numel + 7) / 8 : numel, cus);
-#define MUON_MOM(G, U)                                                                      \
-  do {                                                                                      \
-    if (vec)                                                                                \
-      momentum_kernel<G, U, true><<<grid, 256, 0, s>>>(static_cast<const G*>(grad), mom,    \
-                                                       static_cast<U*>(upd), numel, beta,   \
-                                                       c1, nesterov);                       \
-    else                                                                                    \
-      momentum_kernel<G, U, false><<<grid, 256, 0, s>>>(static_cast<const G*>(grad), mom,   \
-                                                        static_cast<U*>(upd), numel, beta,  \
-                                                        c1, nesterov);                      \
+#define MUON_MOM(G, U)                                                                       \
+  do {                                                                                       \
+    if (vec)                                                                                 \
+      momentum_vec_kernel<G, U><<<vec_grid(numel), EW_BS, 0, s>>>(                           \
+          static_cast<const G*>(grad), mom, static_cast<U*>(upd), numel, beta, c1, nesterov); \
+    else                                                                                     \
+      momentum_scalar_kernel<G, U><<<stream_grid(numel, cus), 256, 0, s>>>(                  \
+          static_cast<const G*>(grad), mom, static_cast<U*>(upd), numel, beta, c1, nesterov); \
   } while (0)
   if (gdt == 1 && udt == 1) MUON_MOM(bf16_t, bf16_t);
   else if (gdt == 1 && udt == 0) MUON_MOM(bf16_t, float);
@@ -180,18 +250,23 @@ hipError_t launch_momentum(hipStream_t s, int cus, const void* grad, int gdt, fl
 
 hipError_t launch_apply(hipStream_t s, int cus, float* master, const void* upd, int udt,
                         void* wbf, int64_t numel, float eta, float decay, int has_wd) {
+  if (numel <= 0) return hipSuccess;
+  if (numel / 8 >= (int64_t{1} << 40)) return hipErrorInvalidValue;  // beyond a 1-D grid
   const bool vec = aligned(master, 16) && aligned(upd, 16) && (wbf == nullptr || aligned(wbf, 16));
-  const unsigned grid = stream_grid(vec ? (numel + 7) / 8 : numel, cus);
   bf16_t* wb = static_cast<bf16_t*>(wbf);
-#define MUON_APPLY(U, V, B)                                                                 \
-  apply_kernel<U, V, B><<<grid, 256, 0, s>>>(master, static_cast<const U*>(upd), wb, numel, \
-                                             eta, decay, has_wd)
+#define MUON_APPLY(U, B)                                                                         \
+  do {                                                                                           \
+    if (vec)                                                                                     \
+      apply_vec_kernel<U, B><<<vec_grid(numel), EW_BS, 0, s>>>(                                   \
+          master, static_cast<const U*>(upd), wb, numel, eta, decay, has_wd);                    \
+    else                                                                                         \
+      apply_scalar_kernel<U, B><<<stream_grid(numel, cus), 256, 0, s>>>(                         \
+          master, static_cast<const U*>(upd), wb, numel, eta, decay, has_wd);                    \
+  } while (0)
   if (udt == 1) {
-    if (vec) { if (wb) MUON_APPLY(bf16_t, true, true); else MUON_APPLY(bf16_t, true, false); }
-    else { if (wb) MUON_APPLY(bf16_t, false, true); else MUON_APPLY(bf16_t, false, false); }
+    if (wb) MUON_APPLY(bf16_t, true); else MUON_APPLY(bf16_t, false);
   } else {
-    if (vec) { if (wb) MUON_APPLY(float, true, true); else MUON_APPLY(float, true, false); }
-    else { if (wb) MUON_APPLY(float, false, true); else MUON_APPLY(float, false, false); }
+    if (wb) MUON_APPLY(float, true); else MUON_APPLY(float, false);
   }
 #undef MUON_APPLY
   return hipGetLastError();

@@ -421,7 +421,6 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   na.unit_elems = unit_elems;
   na.units = L.units;
   na.parts = L.parts;
-  na.chunk = L.chunk;
   na.partial = partial;
   na.scale = scale;
   na.zflag = zflag;

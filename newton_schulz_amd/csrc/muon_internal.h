@@ -38,7 +38,6 @@ struct NsNormArgs {
   int64_t unit_elems;
   int64_t units;
   int parts;           // partial sums per unit
-  int64_t chunk;       // elements per partial (multiple of 8)
   double* partial;     // [units][parts]
   float* scale;        // [units] : 1 / (||Y||_F + eps)
   int* zflag;          // [units] : ||Y||_F == 0

@@ -4,8 +4,8 @@
 // FSDP" (section "Memory control", item 4) advises keeping the normalisation
 // scalars in FP32 even when the buffers are BF16.  Here the squares are formed
 // exactly (bf16^2 fits fp32; fp32^2 fits fp64) and summed in fp64 in a fixed
-// order: per thread strided, then a fixed shared-memory tree, then the parts
-// of a unit in index order.  No atomics take part in the sum, so the scale is
+// order: per thread over its interleaved pieces, then a fixed shared-memory
+// tree, then the parts of a unit in index order.  No atomics take part in the sum, so the scale is
 // bit-reproducible.  The scale 1/(||Y|| + eps) is folded into the first
 // iteration's epilogues instead of rewriting Y.
 #include "muon_device.h"
@@ -15,67 +15,73 @@ using muon::bf16_t;
 
 namespace {
 
+// The elements of a unit are cut into pieces of 256 groups of 8 (one group
+// per thread); workgroup p of a unit's P takes pieces p, p + P, p + 2 P, ...
+// At any moment the workgroups of a unit read neighbouring pieces, so the
+// grid streams through each unit as a few moving windows (much friendlier to
+// HBM pages than P separate contiguous runs).  The order of every sum depends
+// on the unit size and P only.
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void norm_partial_kernel(NsNormArgs a) {
   const int64_t u = blockIdx.y;
-  const int p = blockIdx.x;
+  const int64_t p = blockIdx.x, P = a.parts;
   const T* base = reinterpret_cast<const T*>(mat_at(a.in, u));
-  const int64_t start = static_cast<int64_t>(p) * a.chunk;
-  int64_t end = start + a.chunk;
-  if (end > a.unit_elems) end = a.unit_elems;
+  const int64_t ue = a.unit_elems;
   double acc = 0.0;
   if (VEC) {
-    // start is a multiple of 8; full 8-element groups first
-    const int64_t nfull = (end > start) ? (end - start) / 8 : 0;
-    // four groups per trip, all loaded before the first use (more bytes in
-    // flight per thread); a group past the chunk contributes zeros
-    constexpr int U = 4;
-    for (int64_t g0 = threadIdx.x; g0 < nfull; g0 += 256 * U) {
+    const int64_t ng = ue / 8;  // full 8-element groups
+    // U pieces per trip, all loaded before the first use (a part of ~32K
+    // elements is one trip in bf16, two in fp32); a group past the unit
+    // contributes zeros.  Within a group the eight squares are added as a
+    // fixed pairwise tree.
+    constexpr int U = sizeof(T) == 2 ? 16 : 8;
+    for (int64_t q0 = p; q0 * 256 < ng; q0 += U * P) {
       if (sizeof(T) == 2) {
         uint4 v[U];
 #pragma unroll
         for (int r = 0; r < U; ++r) {
-          const int64_t g = g0 + 256 * r;
-          v[r] = g < nfull ? *reinterpret_cast<const uint4*>(base + start + 8 * g)
-                           : make_uint4(0, 0, 0, 0);
+          const int64_t g = (q0 + r * P) * 256 + threadIdx.x;
+          v[r] = g < ng ? *reinterpret_cast<const uint4*>(base + 8 * g) : make_uint4(0, 0, 0, 0);
         }
 #pragma unroll
         for (int r = 0; r < U; ++r) {
           const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-          double d = 0.0;
+          double q[8];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float lo = __uint_as_float(w[i] << 16), hi = __uint_as_float(w[i] & 0xffff0000u);
-            d += static_cast<double>(lo * lo);
-            d += static_cast<double>(hi * hi);
+            q[2 * i] = static_cast<double>(lo * lo);
+            q[2 * i + 1] = static_cast<double>(hi * hi);
           }
-          acc += d;
+          acc += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
         }
       } else {
         float4 x[U], y[U];
 #pragma unroll
         for (int r = 0; r < U; ++r) {
-          const int64_t g = g0 + 256 * r;
-          const float4* q = reinterpret_cast<const float4*>(base + start + 8 * g);
-          x[r] = g < nfull ? q[0] : make_float4(0.f, 0.f, 0.f, 0.f);
-          y[r] = g < nfull ? q[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+          const int64_t g = (q0 + r * P) * 256 + threadIdx.x;
+          const float4* f = reinterpret_cast<const float4*>(base + 8 * g);
+          x[r] = g < ng ? f[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+          y[r] = g < ng ? f[1] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
 #pragma unroll
         for (int r = 0; r < U; ++r) {
           const float v[8] = {x[r].x, x[r].y, x[r].z, x[r].w, y[r].x, y[r].y, y[r].z, y[r].w};
-          double d = 0.0;
+          double q[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) d += static_cast<double>(v[i]) * static_cast<double>(v[i]);
-          acc += d;
+          for (int i = 0; i < 8; ++i) q[i] = static_cast<double>(v[i]) * static_cast<double>(v[i]);
+          acc += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
         }
       }
     }
-    for (int64_t e = start + 8 * nfull + threadIdx.x; e < end; e += 256) {
-      const double v = static_cast<double>(muon::Elem<T>::load(base + e));
-      acc += v * v;
+    if (p == 0) {  // the last ue % 8 elements
+      for (int64_t e = 8 * ng + threadIdx.x; e < ue; e += 256) {
+        const double v = static_cast<double>(muon::Elem<T>::load(base + e));
+        acc += v * v;
+      }
     }
   } else {
-    for (int64_t e = start + threadIdx.x; e < end; e += 256) {
+    for (int64_t e = p * 256 + threadIdx.x; e < ue; e += P * 256) {
       const double v = static_cast<double>(muon::Elem<T>::load(base + e));
       acc += v * v;
     }
@@ -91,11 +97,18 @@ __global__ __launch_bounds__(256) void norm_partial_kernel(NsNormArgs a) {
   if (threadIdx.x == 0) a.partial[u * a.parts + p] = red[0];
 }
 
+// One wave per unit: lane l adds parts l, l + 64, l + 128, ... in order, then
+// an xor butterfly adds the 64 lane sums (both partners of a step form the
+// same sum, so every lane ends with the same, fixed-order total).
 __global__ __launch_bounds__(256) void norm_finalize_kernel(NsNormArgs a) {
-  const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t u = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
   if (u >= a.units) return;
   double s = 0.0;
-  for (int p = 0; p < a.parts; ++p) s += a.partial[u * a.parts + p];
+  for (int p = lane; p < a.parts; p += 64) s += a.partial[u * a.parts + p];
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) s += __shfl_xor(s, k, 64);
+  if (lane != 0) return;
   const double nrm = sqrt(s);
   a.scale[u] = static_cast<float>(1.0 / (nrm + static_cast<double>(a.eps)));
   a.zflag[u] = (s == 0.0) ? 1 : 0;
@@ -144,7 +157,7 @@ hipError_t launch_norm(hipStream_t s, const NsNormArgs& a, int io_bf16, bool vec
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    norm_finalize_kernel<<<static_cast<unsigned>((c.units + 255) / 256), 256, 0, s>>>(c);
+    norm_finalize_kernel<<<static_cast<unsigned>((c.units + 3) / 4), 256, 0, s>>>(c);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -14,8 +14,7 @@
 //   partial  double per unit and part       norm partial sums
 struct NsLayout {
   int64_t units = 0, ur = 0, uc = 0, m = 0, n = 0;
-  int parts = 1;
-  int64_t chunk = 0;
+  int parts = 1;  // norm partial sums per unit
   size_t xa = 0, xb = 0, a = 0, b = 0, scale = 0, zflag = 0, partial = 0, total = 0;
 };
 

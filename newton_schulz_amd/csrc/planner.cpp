@@ -67,7 +67,6 @@ bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* 
   chunk = (chunk + 7) / 8 * 8;
   parts = (ue + chunk - 1) / chunk;
   l.parts = static_cast<int>(parts);
-  l.chunk = chunk;
   const size_t U = static_cast<size_t>(l.units);
   const size_t xbytes = align_up(U * static_cast<size_t>(l.m * l.n) * e);
   const size_t abytes = align_up(U * static_cast<size_t>(l.m * l.m) * e);

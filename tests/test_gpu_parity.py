@@ -57,7 +57,11 @@ def gen(seed):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("gdt,udt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
                                      (torch.bfloat16, torch.float32), (torch.float32, torch.bfloat16)])
-@pytest.mark.parametrize("numel,offset", [(1, 0), (4099, 0), (1 << 20, 0), (100003, 1), (8 * 1000 + 5, 3)])
+# aligned sizes take the one-shot vector path (4096 elements per workgroup, a
+# partial last workgroup and a scalar tail of numel % 8); offsets that break
+# 16-byte alignment take the grid-stride scalar path
+@pytest.mark.parametrize("numel,offset", [(1, 0), (4099, 0), (1 << 20, 0), (3 * 4096 + 8 * 37 + 5, 0),
+                                          (100003, 1), (8 * 1000 + 5, 3)])
 @pytest.mark.parametrize("nesterov", [True, False])
 def test_momentum_bitexact(ctx, gdt, udt, numel, offset, nesterov):
     say(f"momentum {gdt} -> {udt} numel={numel} offset={offset} nesterov={nesterov}")
@@ -77,7 +81,7 @@ def test_momentum_bitexact(ctx, gdt, udt, numel, offset, nesterov):
 
 
 @pytest.mark.parametrize("udt", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("numel,offset", [(7, 0), (1 << 20, 0), (65541, 1)])
+@pytest.mark.parametrize("numel,offset", [(7, 0), (1 << 20, 0), (3 * 4096 + 8 * 37 + 5, 0), (65541, 1)])
 @pytest.mark.parametrize("wd,want_bf16", [(0.0, True), (0.1, False), (0.0, False)])
 def test_apply_bitexact(ctx, udt, numel, offset, wd, want_bf16):
     say(f"apply {udt} numel={numel} offset={offset} wd={wd} bf16={want_bf16}")
