@@ -79,15 +79,16 @@ def unit_list(w):
     return units
 
 
-def traffic_record(kernel_src: str):
+def traffic_record(*kernel_src: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, or None when missing or taken on a different source."""
+    counter summary, or None when missing or taken on different kernel code
+    (the kernel file and its local headers)."""
     path = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_4b.json")
     if not os.path.exists(path):
         return None
     from newton_schulz_amd.prof import source_fingerprint
     rec = json.load(open(path))
-    if rec.get("source_code_sha256_16") != source_fingerprint(kernel_src):
+    if rec.get("source_code_sha256_16") != source_fingerprint(*kernel_src):
         return None
     return round(rec.get("hbm_bytes_per_launch"))
 
@@ -269,7 +270,9 @@ def main():
         f_upd = ex["update"]
         if n_upd > 0 and t_upd > 0:
             achieved = f_upd / (t_upd * 1e-3) / 1e12
-            traffic = traffic_record(os.path.join(ROOT, "newton_schulz_amd", "csrc", "ns_gemm_mfma.hip"))
+            csrc = os.path.join(ROOT, "newton_schulz_amd", "csrc")
+            traffic = traffic_record(os.path.join(csrc, "ns_gemm_mfma.hip"),
+                                     os.path.join(csrc, "ns_mfma_common.h"))
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                         "traffic": traffic, "kernel": "ns_gemm_mfma_kernel (update X' = B' X, B' = a I + b A + c A A)",

@@ -61,6 +61,19 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
  *     2 m <= n and the quintic iteration on the others (F32: always). */
 typedef enum { MUON_NS_QUINTIC = 0, MUON_NS_GRAM = 1 } muon_ns_method_t;
 
+/* Whole-iteration fusion of the quintic iteration for small units: a wide
+ * BF16 unit with m <= 128 (e.g. the 128 x n heads of per-head Muon, RFC
+ * section 4D) can run every iteration in one launch, one workgroup per unit
+ * holding A and B in on-chip memory; the Gram product of the next iteration
+ * is accumulated while the update is stored, so the iterate is read once
+ * and written once per iteration.  Results are bit-identical to the
+ * unfused kernels.  AUTO fuses when the call has at least as many units as
+ * the device has compute units (every CU gets a unit); ON whenever
+ * eligible; OFF never.  Not eligible: tall units, m > 128, F32 compute,
+ * MUON_NS_GRAM, and outputs that overlap the inputs other than unit for
+ * unit in place. */
+typedef enum { MUON_FUSE_AUTO = 0, MUON_FUSE_OFF = 1, MUON_FUSE_ON = 2 } muon_fuse_t;
+
 /* Newton-Schulz parameters.  The quintic iteration is the one the DeepSpeed
  * RFC "Enable Correct and High-Performance Muon Optimizer under ZeRO CPU
  * Offload" calls the current default (section 5, Roadmap), run for 5~6
@@ -79,6 +92,7 @@ typedef struct {
   int32_t compute;   /* muon_dtype_t: BF16 = bf16 MFMA with fp32 accumulate,
                         F32 = fp32 verification mode */
   int32_t method;    /* muon_ns_method_t, default MUON_NS_QUINTIC */
+  int32_t fuse;      /* muon_fuse_t, default MUON_FUSE_AUTO */
 } muon_ns_params_t;
 
 /* Geometry of one weight matrix (RFC section 4A: keep the 2D shape and head
@@ -248,7 +262,8 @@ typedef enum {
   MUON_K_UPDATE = 4,
   MUON_K_APPLY = 5,
   MUON_K_PROD = 6,   /* m x m products of MUON_NS_GRAM (P_k Q_k, P_k A_k, (P_k A_k) P_k) */
-  MUON_K_COUNT = 7
+  MUON_K_FUSED = 7,  /* whole-iteration launches of small units (muon_fuse_t) */
+  MUON_K_COUNT = 8
 } muon_kernel_class_t;
 
 muon_status_t muon_timing_enable(muon_ctx_t* ctx, int32_t enable, int32_t capacity);

@@ -10,7 +10,7 @@ LIB_PATH = os.path.join(HERE, "libmuon.so")
 MUON_OK, MUON_EINVAL, MUON_ESHAPE, MUON_EDTYPE, MUON_EWORKSPACE, MUON_EHIP, MUON_ENOMEM = range(7)
 MUON_F32, MUON_BF16 = 0, 1
 MUON_CAP_FULL_BYTES, MUON_CAP_WORKSPACE = 0, 1
-KERNEL_CLASSES = ["momentum", "norm", "gram", "symsq", "update", "apply", "prod"]
+KERNEL_CLASSES = ["momentum", "norm", "gram", "symsq", "update", "apply", "prod", "fused"]
 
 # every symbol include/muon.h declares
 EXPORTS = [
@@ -25,7 +25,7 @@ EXPORTS = [
 class NsParams(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
                 ("c", ctypes.c_float), ("eps", ctypes.c_float), ("compute", ctypes.c_int32),
-                ("method", ctypes.c_int32)]
+                ("method", ctypes.c_int32), ("fuse", ctypes.c_int32)]
 
 
 class Shape(ctypes.Structure):

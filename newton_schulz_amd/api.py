@@ -46,13 +46,15 @@ def _check(t: torch.Tensor, name: str, device: torch.device):
         raise ValueError(f"{name} must be contiguous")
 
 
+NS_FUSE = {"auto": 0, "off": 1, "on": 2}
 NS_METHODS = {"quintic": 0, "gram": 1}
 
 
 def ns_params(steps: int = 5, a: float = 3.4445, b: float = -4.7750, c: float = 2.0315,
-              eps: float = 1e-7, compute: str = "bf16", method: str = "quintic") -> NsParams:
+              eps: float = 1e-7, compute: str = "bf16", method: str = "quintic",
+              fuse: str = "auto") -> NsParams:
     return NsParams(steps, a, b, c, eps, MUON_BF16 if compute == "bf16" else MUON_F32,
-                    NS_METHODS[method])
+                    NS_METHODS[method], NS_FUSE[fuse])
 
 
 def ns_workspace_bytes(rows: int, cols: int, count: int, head_rows: int = 0,

@@ -83,8 +83,7 @@ __device__ __forceinline__ void momentum_one(float g, float& m, float& u, float 
 }
 
 // one-shot vector path: EW_U groups of 8 elements per thread, EW_BS threads
-constexpr int EW_BS = 256, EW_U = 2;
-constexpr int64_t EW_BLOCK = 8 * EW_U * EW_BS;  // elements per workgroup
+constexpr int EW_BS = 256, EW_U = 2;  // 4096 elements per workgroup
 
 template <typename G, typename U>
 __global__ __launch_bounds__(EW_BS) void momentum_vec_kernel(const G* __restrict__ grad,
@@ -206,7 +205,7 @@ __global__ __launch_bounds__(256) void apply_scalar_kernel(float* __restrict__ m
   }
 }
 
-// one workgroup per EW_BLOCK elements (at least one, for the scalar tail)
+// one workgroup per 4096 elements (at least one, for the scalar tail)
 inline unsigned vec_grid(int64_t numel) {
   const int64_t blocks = (numel / 8 + EW_U * EW_BS - 1) / (EW_U * EW_BS);
   return static_cast<unsigned>(blocks < 1 ? 1 : blocks);

@@ -92,6 +92,24 @@ bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
   return na && nb && x < y + nb && y < x + na;
 }
 
+// Does some out[j] (bytes long) overlap an in[k] other than in[j] == out[j]
+// exactly?  Inputs sorted by address; each output checks the inputs starting
+// less than `bytes` away.
+bool cross_overlap(const void* const* in, const void* const* out, int64_t count, int64_t bytes) {
+  std::vector<std::pair<uintptr_t, int64_t>> v(static_cast<size_t>(count));
+  for (int64_t i = 0; i < count; ++i) v[i] = {reinterpret_cast<uintptr_t>(in[i]), i};
+  std::sort(v.begin(), v.end());
+  const uintptr_t b = static_cast<uintptr_t>(bytes);
+  for (int64_t j = 0; j < count; ++j) {
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out[j]);
+    const uintptr_t lo = o >= b ? o - b + 1 : 0;
+    auto it = std::lower_bound(v.begin(), v.end(), std::make_pair(lo, int64_t{-1}));
+    for (; it != v.end() && it->first < o + b; ++it)
+      if (it->second != j || it->first != o) return true;
+  }
+  return false;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,6 +138,7 @@ void muon_ns_params_default(muon_ns_params_t* p) {
   p->eps = 1e-7f;
   p->compute = MUON_BF16;
   p->method = MUON_NS_QUINTIC;
+  p->fuse = MUON_FUSE_AUTO;
 }
 
 size_t muon_ctx_workspace_bytes(const muon_ctx_t* ctx) { return ctx ? ctx->ws_bytes : 0; }
@@ -330,6 +349,8 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   if (prm->steps < 0 || !(prm->eps >= 0.0f)) return fail(c, MUON_EINVAL, "steps/eps");
   if (prm->method != MUON_NS_QUINTIC && prm->method != MUON_NS_GRAM)
     return fail(c, MUON_EINVAL, "method");
+  if (prm->fuse != MUON_FUSE_AUTO && prm->fuse != MUON_FUSE_OFF && prm->fuse != MUON_FUSE_ON)
+    return fail(c, MUON_EINVAL, "fuse");
   NsLayout L;
   if (!ns_layout(shape, count, prm->compute, &L)) return fail(c, MUON_ESHAPE, "shape");
   if (count == 0) return MUON_OK;
@@ -444,6 +465,23 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     tstop(c, s, k);
     return r;
   };
+  // Does the output touch the input?  `alias`: the spans of the inputs and
+  // the outputs overlap at all (conservative).
+  bool alias = false;
+  {
+    const int64_t call_bytes = unit_bytes * per;
+    const char *ilo = nullptr, *ihi = nullptr, *olo = nullptr, *ohi = nullptr;
+    for (int64_t i = 0; i < count; ++i) {
+      const char* pi = static_cast<const char*>(mats[i]);
+      const char* po = static_cast<const char*>(outp[i]);
+      alias = alias || pi == po;
+      ilo = (i == 0 || pi < ilo) ? pi : ilo;
+      ihi = (i == 0 || pi + call_bytes > ihi) ? pi + call_bytes : ihi;
+      olo = (i == 0 || po < olo) ? po : olo;
+      ohi = (i == 0 || po + call_bytes > ohi) ? po + call_bytes : ohi;
+    }
+    alias = alias || ranges_overlap(ilo, ihi - ilo, olo, ohi - olo);
+  }
   // The Gram form squares the singular values into A_0; in bf16 that loses
   // the small ones once m nears n (relative error ~1e-1 on square Gaussian
   // inputs against ~1e-2 for the quintic), so bf16 runs it only on units with
@@ -496,19 +534,6 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     }
     // X = s Q X_0 (tall: Y Q).  Written straight to the output unless the
     // output overlaps the input, then through the free iterate region.
-    const int64_t call_bytes = unit_bytes * per;
-    const char *ilo = nullptr, *ihi = nullptr, *olo = nullptr, *ohi = nullptr;
-    bool alias = false;
-    for (int64_t i = 0; i < count; ++i) {
-      const char* pi = static_cast<const char*>(mats[i]);
-      const char* po = static_cast<const char*>(outp[i]);
-      alias = alias || pi == po;
-      ilo = (i == 0 || pi < ilo) ? pi : ilo;
-      ihi = (i == 0 || pi + call_bytes > ihi) ? pi + call_bytes : ihi;
-      olo = (i == 0 || po < olo) ? po : olo;
-      ohi = (i == 0 || po + call_bytes > ohi) ? po + call_bytes : ohi;
-    }
-    alias = alias || ranges_overlap(ilo, ihi - ilo, olo, ohi - olo);
     const MatRef freeX = (Q.base == R2.base) ? XB : XA;
     NsGemmArgs ua{};
     ua.dst = alias ? freeX : ot.ref;
@@ -536,6 +561,32 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
       if (e != hipSuccess) return hip_fail(c, e, "copy launch");
     }
     return MUON_OK;
+  }
+
+  // Small wide units: every iteration in one launch.  A workgroup writes only
+  // its own unit, so an output may be its own input but may not touch any
+  // other matrix's input.
+  const bool small_ok = mfma && !tall && m <= 128 && prm->fuse != MUON_FUSE_OFF &&
+                        (!alias || !cross_overlap(mats, outp, count, unit_bytes * per));
+  if (small_ok && (prm->fuse == MUON_FUSE_ON || L.units >= c->cus)) {
+    NsSmallArgs fa{};
+    fa.src = in.ref;
+    fa.dst = ot.ref;
+    fa.xa = XA;
+    fa.xb = XB;
+    fa.m = static_cast<int>(m);
+    fa.n = static_cast<int>(n);
+    fa.steps = prm->steps;
+    fa.units = L.units;
+    fa.scale = scale;
+    fa.zflag = zflag;
+    fa.ca = prm->a;
+    fa.cb = prm->b;
+    fa.cc = prm->c;
+    const long k = tstart(c, s, MUON_K_FUSED);
+    e = launch_ns_small(s, fa);
+    tstop(c, s, k);
+    return e == hipSuccess ? MUON_OK : hip_fail(c, e, "fused launch");
   }
 
   for (int k = 0; k < prm->steps; ++k) {

@@ -45,6 +45,20 @@ struct NsNormArgs {
   float eps;
 };
 
+// The whole quintic iteration of wide units with m <= 128 in one launch
+// (ns_small.hip): src = the units Y (m x n, rows contiguous), dst = the
+// result, xa / xb = two iterate regions of m x n per unit.
+struct NsSmallArgs {
+  MatRef src, dst, xa, xb;
+  int m, n, steps;
+  int64_t units;
+  const float* scale;  // per-unit s = 1 / (||Y||_F + eps)
+  const int* zflag;    // per-unit "norm is zero" flag, or nullptr
+  float ca, cb, cc;    // quintic coefficients a, b, c
+};
+
+hipError_t launch_ns_small(hipStream_t s, const NsSmallArgs& a);
+
 hipError_t launch_momentum(hipStream_t s, int cus, const void* grad, int gdt, float* mom,
                            void* upd, int udt, int64_t numel, float beta, float c1,
                            int nesterov);

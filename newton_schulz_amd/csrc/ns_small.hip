@@ -1,0 +1,336 @@
+// The whole quintic Newton-Schulz iteration of units with m <= 128 in one
+// launch (bf16 MFMA, fp32 accumulation), e.g. the per-head 128 x 2560 q/k/v
+// matrices of per-head Muon.
+//
+// One workgroup owns one unit for all iterations: 4 waves, 2 x 2 over a
+// 128 x 128 output, 64 x 64 each (the layout of the 128 x 128 tiles of the
+// separate product launches).  A and B' stay in LDS as bf16; the m x n
+// iterate streams through LDS in 128-column blocks.  With X_0 = s Y
+// (s = 1 / (||Y||_F + eps)) folded into the first products:
+//   A_0 = s^2 Y Y^T                          one pass over the input
+//   per iteration k:
+//     B' = a I + b A_k + c A_k A_k           K = 128, from LDS
+//     per column block j:  X'_j = f B' X_j   (f = s when k = 0, else 1)
+//                          store X'_j;  A_{k+1} += X'_j X'_j^T
+// The Gram product of the next iteration is accumulated from the bf16 block
+// just stored, so each iteration reads the iterate once and writes it once
+// (separate launches read it twice), and no product pays a launch and a
+// tile prologue of its own.  Rounding points (A, B', every iterate in bf16),
+// the MFMA shape and the order of every sum are those of the separate
+// launches; A and B' take their lower triangle from the upper one as the
+// mirrored tiles there do.
+//
+// Units are wide (m = rows <= n = cols), rows contiguous (ld = n), with
+// m % 8 == n % 8 == 0; rows past m and columns past n read as zeros.
+#include "ns_mfma_common.h"
+
+namespace {
+
+constexpr int SM = 128;            // rows and columns of A and B' (m padded)
+constexpr int NWV = 4;             // waves
+constexpr int HALF = SM * 64 * 2;  // one 64-k half of a 128-row K-contiguous tile
+constexpr int SLAB = SM * SM * 2;  // a 128 x 128 bf16 block
+constexpr int NGR = SM / (8 * NWV);   // row-slab DMA instructions per wave (128 rows x 64 k)
+constexpr int NGC = SM / (4 * NWV);   // column-block DMA instructions per wave (128 k x 128 cols)
+constexpr int NST = SM * SM / 8 / (64 * NWV);  // 16-byte stores per lane per block
+
+// Element (i, j) of a 128 x 128 bf16 matrix kept as two 64-column halves in
+// the K-contiguous tile layout (columns are the contraction index).
+__device__ __forceinline__ char* rt_at(char* t, int i, int j) {
+  return t + (j >> 6) * HALF + rt_off<64>(i, (j & 63) >> 3) + ((j & 7) << 1);
+}
+
+// MFMA operand: rows rb .. rb + 31, k = 16 kk + 8 (lane / 32) + 0..7, kk < 8
+__device__ __forceinline__ bf16x8_t rt_frag(const char* t, int rb, int kk, int lane) {
+  return *reinterpret_cast<const bf16x8_t*>(t + (kk >> 2) * HALF +
+                                            rt_off<64>(rb + (lane & 31), 2 * (kk & 3) + (lane >> 5)));
+}
+
+// MFMA operand from a K-major 128 x 128 block (k = memory row): columns
+// rb .. rb + 31, four consecutive k per ds_read_b64_tr_b16, kk < 8
+__device__ __forceinline__ bf16x8_t kt_frag(const char* t, int rb, int kk, int lane) {
+  const int gq = lane >> 4, j = lane & 15;
+  const int col = rb + 16 * (gq & 1) + 4 * (j & 3);
+  const int k = 16 * kk + 8 * (gq >> 1) + (j >> 2);
+  const u32x2_t lo = __builtin_bit_cast(u32x2_t, ld_tr16(t + kt_off<SM>(k, col)));
+  const u32x2_t hi = __builtin_bit_cast(u32x2_t, ld_tr16(t + kt_off<SM>(k + 4, col)));
+  const u32x4_t v = {lo.x, lo.y, hi.x, hi.y};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+struct Acc {
+  f32x16_t v[2][2];
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni) v[mi][ni] = (f32x16_t)(0.0f);
+  }
+  // acc += P_M P_N^T over one k16 step; fa: N side, fb: M side
+  __device__ __forceinline__ void mma(const bf16x8_t (&fa)[2], const bf16x8_t (&fb)[2]) {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        v[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ni], fb[mi], v[mi][ni], 0, 0, 0);
+  }
+};
+
+// Lane l holds row wm 64 + mi 32 + l % 32 and, per register group g, columns
+// wn 64 + ni 32 + 8 g + 4 (l / 32) + 0..3 of the accumulated product.
+template <typename F>
+__device__ __forceinline__ void for_acc(int wm, int wn, int lane, F&& f) {
+  static_for<2>([&](auto MI) {
+    static_for<2>([&](auto NI) {
+      static_for<4>([&](auto G) {
+        constexpr int mi = decltype(MI)::value, ni = decltype(NI)::value, g = decltype(G)::value;
+        f(mi, ni, g, wm * 64 + mi * 32 + (lane & 31), wn * 64 + ni * 32 + 8 * g + 4 * (lane >> 5));
+      });
+    });
+  });
+}
+
+__device__ __forceinline__ uint2 pack4(const float (&v)[4]) {
+  uint2 w;
+  w.x = muon::pack_bf16x2(v[0], v[1]);
+  w.y = muon::pack_bf16x2(v[2], v[3]);
+  return w;
+}
+
+// lower triangle <- upper triangle (the mirrored tiles of separate launches)
+__device__ __forceinline__ void mirror_lower(char* t, int tid) {
+  for (int e = tid; e < SM * SM; e += 64 * NWV) {
+    const int i = e >> 7, j = e & (SM - 1);
+    if (i > j) *reinterpret_cast<uint16_t*>(rt_at(t, i, j)) = *reinterpret_cast<const uint16_t*>(rt_at(t, j, i));
+  }
+}
+
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
+  __shared__ __attribute__((aligned(1024))) char bp[2 * HALF];  // B'
+  __shared__ __attribute__((aligned(1024))) char am[2 * HALF];  // A; the X' block staging
+  __shared__ __attribute__((aligned(1024))) char s0[SLAB];      // iterate blocks / row slabs
+  __shared__ __attribute__((aligned(1024))) char s1[SLAB];
+  __shared__ __attribute__((aligned(1024))) char s2[SLAB];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t u = blockIdx.x;
+  const int m = a.m, n = a.n;
+  const uint32_t ubytes = static_cast<uint32_t>(static_cast<int64_t>(m) * n * 2);
+  const int nb = (n + SM - 1) / SM;  // column blocks
+
+  // 16-byte row-contiguous stores of one 128 x 128 block (zeros when src_tile
+  // is null); chunks outside the unit get an offset the hardware drops
+  auto store_block = [&](const bf16_t* dst, int c0, const char* src_tile) {
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(dst, ubytes);
+#pragma unroll
+    for (int it = 0; it < NST; ++it) {
+      const int e = tid + 64 * NWV * it;
+      const int row = e >> 4, ch = e & 15;
+      const u32x4_t val = src_tile ? *reinterpret_cast<const u32x4_t*>(src_tile + (ch >> 3) * HALF +
+                                                                        rt_off<64>(row, ch & 7))
+                                   : u32x4_t{0u, 0u, 0u, 0u};
+      const uint32_t off = (row < m && c0 + 8 * ch < n)
+                               ? static_cast<uint32_t>((static_cast<int64_t>(row) * n + c0 + 8 * ch) * 2)
+                               : kOOB;
+      __builtin_amdgcn_raw_buffer_store_b128(val, dr, off, 0, 0);
+    }
+  };
+
+  const bf16_t* y = uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.src, u)));
+  const bf16_t* out = uniform_ptr(reinterpret_cast<const bf16_t*>(mat_at(a.dst, u)));
+  if (a.zflag != nullptr && a.zflag[u] != 0) {  // a zero unit's result is exactly zero
+    for (int c = 0; c < nb; ++c) store_block(out, c * SM, nullptr);
+    return;
+  }
+  const float s = a.scale[u];
+
+  // ---- A_0 = s^2 Y Y^T: 128-row x 64-k slabs of Y, two stage buffers
+  {
+    const u32x4_t rs = rsrc_words(y, ubytes);
+    uint32_t base[NGR];
+    int kc[NGR];
+#pragma unroll
+    for (int q = 0; q < NGR; ++q) {
+      const int row = 8 * (wave + NWV * q) + (lane >> 3);
+      const int lc = (lane & 7) ^ rt_swz<64>(row);
+      kc[q] = 8 * lc;
+      base[q] = row < m ? static_cast<uint32_t>((static_cast<int64_t>(row) * n + 8 * lc) * 2) : kOOB;
+    }
+    auto issue = [&](char* st, int k0) {
+#pragma unroll
+      for (int q = 0; q < NGR; ++q)
+        dma16_asm(rs, st + (wave + NWV * q) * 1024, k0 + kc[q] < n ? base[q] : kOOB,
+                  static_cast<uint32_t>(k0 * 2));
+    };
+    Acc acc;
+    acc.zero();
+    const int KT = (n + 63) / 64;
+    issue(s0, 0);
+    issue(s1, 64);
+    for (int kt = 0; kt < KT; ++kt) {
+      char* st = (kt & 1) ? s1 : s0;
+      // this wave's loads of stage kt have landed (stage kt + 1 may fly)
+      asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NGR) : "memory");
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        bf16x8_t fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          fa[i] = rt_frag(st, wn * 64 + i * 32, kk, lane);
+          fb[i] = rt_frag(st, wm * 64 + i * 32, kk, lane);
+        }
+        acc.mma(fa, fb);
+      }
+      barrier_lds();  // every wave is done with stage kt's buffer
+      issue(st, (kt + 2) * 64);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const float s2 = s * s;
+    for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = s2 * acc.v[mi][ni][4 * g + q];
+      *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
+    });
+    barrier_lds();
+    mirror_lower(am, tid);
+    barrier_lds();
+  }
+
+  for (int k = 0; k < a.steps; ++k) {
+    const bool last = k + 1 == a.steps;
+    // ---- B' = a I + b A + c A A
+    {
+      Acc acc;
+      acc.zero();
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        bf16x8_t fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          fa[i] = rt_frag(am, wn * 64 + i * 32, kk, lane);
+          fb[i] = rt_frag(am, wm * 64 + i * 32, kk, lane);
+        }
+        acc.mma(fa, fb);
+      }
+      for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
+        const uint2 w = *reinterpret_cast<const uint2*>(rt_at(am, i, j));
+        const float e[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = a.cb * e[q] + a.cc * acc.v[mi][ni][4 * g + q];
+          if (i == j + q) v[q] += a.ca;
+        }
+        *reinterpret_cast<uint2*>(rt_at(bp, i, j)) = pack4(v);
+      });
+      barrier_lds();
+      mirror_lower(bp, tid);
+      barrier_lds();
+    }
+
+    // ---- X_{k+1} = f B' X_k block by block, A_{k+1} accumulated on the way
+    const bf16_t* xs = k == 0 ? y : uniform_ptr(reinterpret_cast<const bf16_t*>(
+                                        mat_at(((k - 1) & 1) ? a.xb : a.xa, u)));
+    const bf16_t* xd = last ? out : uniform_ptr(reinterpret_cast<const bf16_t*>(
+                                        mat_at((k & 1) ? a.xb : a.xa, u)));
+    const u32x4_t rs = rsrc_words(xs, ubytes);
+    uint32_t base[NGC];
+    int cc[NGC];
+#pragma unroll
+    for (int q = 0; q < NGC; ++q) {
+      const int kr = 4 * (wave + NWV * q) + (lane >> 4);
+      const int col = 8 * ((lane & 15) ^ ((kr & 3) << 2));
+      cc[q] = col;
+      base[q] = kr < m ? static_cast<uint32_t>((static_cast<int64_t>(kr) * n + col) * 2) : kOOB;
+    }
+    auto issue = [&](char* sl, int c0) {
+#pragma unroll
+      for (int q = 0; q < NGC; ++q)
+        dma16_asm(rs, sl + (wave + NWV * q) * 1024, c0 + cc[q] < n ? base[q] : kOOB,
+                  static_cast<uint32_t>(c0 * 2));
+    };
+    const float f = k == 0 ? s : 1.0f;
+    Acc an;  // A_{k+1}
+    an.zero();
+    issue(s0, 0);
+    issue(s1, SM);
+    issue(s2, 2 * SM);
+    for (int c = 0; c < nb; ++c) {
+      char* sl = (c % 3 == 0) ? s0 : ((c % 3 == 1) ? s1 : s2);
+      // wait for this wave's block-c loads; issued after them: blocks c + 1,
+      // c + 2 (8 loads each) and the stores of blocks c - 2, c - 1 (8 each)
+      if (c == 0)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC) : "memory");
+      else if (c == 1)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC + NST) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC + 2 * NST) : "memory");
+      Acc ax;
+      ax.zero();
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        bf16x8_t fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          fa[i] = kt_frag(sl, wn * 64 + i * 32, kk, lane);
+          fb[i] = rt_frag(bp, wm * 64 + i * 32, kk, lane);
+        }
+        ax.mma(fa, fb);
+      }
+      for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = f * ax.v[mi][ni][4 * g + q];
+        *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
+      });
+      barrier_lds();
+      store_block(xd, c * SM, am);
+      if (!last) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          bf16x8_t fa[2], fb[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            fa[i] = rt_frag(am, wn * 64 + i * 32, kk, lane);
+            fb[i] = rt_frag(am, wm * 64 + i * 32, kk, lane);
+          }
+          an.mma(fa, fb);
+        }
+      }
+      barrier_lds();  // block c's buffer and the staging are free again
+      issue(sl, (c + 3) * SM);
+    }
+    // the next iteration reads what this one stored
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (!last) {
+      for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = an.v[mi][ni][4 * g + q];
+        *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
+      });
+      barrier_lds();
+      mirror_lower(am, tid);
+      barrier_lds();
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ns_small(hipStream_t s, const NsSmallArgs& a) {
+  if (a.units <= 0) return hipSuccess;
+  if (a.m < 1 || a.m > SM || a.n < a.m || a.m % 8 || a.n % 8 || a.steps < 1 ||
+      static_cast<int64_t>(a.m) * a.n * 2 >= (int64_t{1} << 31) || a.units > 0x7fffffff)
+    return hipErrorInvalidValue;
+  ns_small_kernel<<<static_cast<unsigned>(a.units), 64 * NWV, 0, s>>>(a);
+  return hipGetLastError();
+}

@@ -19,16 +19,17 @@ import re
 import sys
 
 
-def source_fingerprint(path: str) -> str:
-    """First 16 hex digits of the SHA-256 of a source file with its // comments
-    and blank lines removed: a comment edit keeps a counter record valid, any
-    code change invalidates it."""
+def source_fingerprint(*paths: str) -> str:
+    """First 16 hex digits of the SHA-256 of source files (in the order given)
+    with their // comments and blank lines removed: a comment edit keeps a
+    counter record valid, any code change invalidates it."""
     import hashlib
     lines = []
-    for line in open(path, encoding="utf-8"):
-        code = re.sub(r"//.*", "", line).rstrip()
-        if code:
-            lines.append(code)
+    for path in paths:
+        for line in open(path, encoding="utf-8"):
+            code = re.sub(r"//.*", "", line).rstrip()
+            if code:
+                lines.append(code)
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
@@ -95,7 +96,7 @@ def traffic(a):
     }
     if a.source:
         res["source"] = a.source
-        res["source_code_sha256_16"] = source_fingerprint(a.source)
+        res["source_code_sha256_16"] = source_fingerprint(*a.source)
     json.dump(res, sys.stdout, indent=1)
     print()
 
@@ -115,7 +116,8 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=float, required=True)
     t.add_argument("--copy-kernel", default="copy")
     t.add_argument("--kernel", required=True)
-    t.add_argument("--source", default=None, help="kernel source file to fingerprint")
+    t.add_argument("--source", nargs="+", default=None,
+                   help="kernel source files to fingerprint (the kernel and its local headers)")
     t.add_argument("--label", default=None, help="kernel description stored in the record")
     a = ap.parse_args(argv)
     if a.cmd == "stats":

@@ -62,6 +62,9 @@ def test_struct_and_enum_mirrors_match_header():
     count = int(re.search(r"MUON_K_COUNT\s*=\s*(\d+)", text).group(1))
     assert len(_lib.KERNEL_CLASSES) == count
     assert int(re.search(r"MUON_NS_GRAM\s*=\s*(\d+)", text).group(1)) == 1
+    from newton_schulz_amd.api import NS_FUSE
+    for name, v in NS_FUSE.items():
+        assert int(re.search(rf"MUON_FUSE_{name.upper()}\s*=\s*(\d+)", text).group(1)) == v
 
 
 def test_null_context_rejected():
@@ -69,7 +72,7 @@ def test_null_context_rejected():
     p = _lib.NsParams()
     lib.muon_ns_params_default(ctypes.byref(p))
     assert (p.steps, round(p.a, 4), round(p.b, 4), round(p.c, 4), p.compute) == (5, 3.4445, -4.775, 2.0315, 1)
-    assert p.method == 0
+    assert p.method == 0 and p.fuse == 0
     assert lib.muon_momentum_update(None, None, None, 1, None, None, 1, 10, 0.95, 1) == _lib.MUON_EINVAL
     assert lib.muon_apply(None, None, None, None, 1, None, 10, 0.02, 1.0, 0.0) == _lib.MUON_EINVAL
     assert lib.muon_newton_schulz_batched(None, None, None, 1, _lib.Shape(8, 8, 0), 1, ctypes.byref(p),
