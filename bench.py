@@ -68,14 +68,17 @@ def workload_by_name(name):
     raise SystemExit(f"unknown workload {name}")
 
 
-def unit_list(w):
+def unit_list(w, wide_flag: bool = False):
+    """(m, n) of every Newton-Schulz unit with a nonzero gradient (with
+    wide_flag: (m, n, rows <= cols))."""
     units = []
     for m in w.mats:
         if m.zero_grad:
             continue
         ur = m.head_rows or m.rows
         for _ in range(m.rows // ur):
-            units.append((min(ur, m.cols), max(ur, m.cols)))
+            u = (min(ur, m.cols), max(ur, m.cols))
+            units.append(u + (ur <= m.cols,) if wide_flag else u)
     return units
 
 
@@ -229,12 +232,18 @@ def main():
     # (for the Gram form: quintic-equivalent throughput); the per-class rates
     # use the flops each class actually executed
     value = f_ns / (ms_per_step * 1e-3) / 1e12
-    ex = {"gram": 0, "symsq": 0, "prod": 0, "update": 0}
-    for (m, n) in units:
+    ex = {"gram": 0, "symsq": 0, "prod": 0, "update": 0, "fused": 0}
+    # units the library ran as one fused launch (small wide bf16 units; every
+    # such call in these workloads has a unit per CU)
+    fused_ran = timing and kt["fused"][1] > 0
+    for (m, n, wide) in unit_list(w, wide_flag=True):
         if args.ns_method == "gram" and uses_gram_form(m, n, w.compute):
             fg, fs, fp, fu = ns_flops_gram(m, n, w.ns_steps)
         else:
             (fg, fs, fu), fp = ns_flops(m, n, w.ns_steps), 0
+        if fused_ran and w.compute == "bf16" and wide and m <= 128:
+            ex["fused"] += fg + fs + fp + fu
+            continue
         ex["gram"] += fg
         ex["symsq"] += fs
         ex["prod"] += fp
@@ -254,12 +263,13 @@ def main():
         def tf(f, k):
             t = per_step[k][0]
             return round(f / (t * 1e-3) / 1e12, 2) if t > 0 else None
-        for k in ("gram", "symsq", "prod", "update"):
+        for k in ("gram", "symsq", "prod", "update", "fused"):
             if per_step[k][1] > 0:
                 breakdown[k]["tflops"] = tf(ex[k], k)
-        if per_step["prod"][1] == 0:
-            del breakdown["prod"]
-        ns_ms = sum(per_step[k][0] for k in ("norm", "gram", "symsq", "prod", "update"))
+        for k in ("gram", "symsq", "prod", "update", "fused"):
+            if per_step[k][1] == 0:
+                del breakdown[k]
+        ns_ms = sum(per_step[k][0] for k in ("norm", "gram", "symsq", "prod", "update", "fused"))
         breakdown["newton_schulz"] = {"ms_per_step": round(ns_ms, 4),
                                       "tflops": round(sum(ex.values()) / (ns_ms * 1e-3) / 1e12, 2) if ns_ms else None}
         for k, b in (("momentum", mom_bytes), ("apply", app_bytes)):

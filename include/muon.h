@@ -61,17 +61,18 @@ typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
  *     2 m <= n and the quintic iteration on the others (F32: always). */
 typedef enum { MUON_NS_QUINTIC = 0, MUON_NS_GRAM = 1 } muon_ns_method_t;
 
-/* Whole-iteration fusion of the quintic iteration for small units: a wide
- * BF16 unit with m <= 128 (e.g. the 128 x n heads of per-head Muon, RFC
- * section 4D) can run every iteration in one launch, one workgroup per unit
- * holding A and B in on-chip memory; the Gram product of the next iteration
- * is accumulated while the update is stored, so the iterate is read once
- * and written once per iteration.  Results are bit-identical to the
- * unfused kernels.  AUTO fuses when the call has at least as many units as
- * the device has compute units (every CU gets a unit); ON whenever
- * eligible; OFF never.  Not eligible: tall units, m > 128, F32 compute,
- * MUON_NS_GRAM, and outputs that overlap the inputs other than unit for
- * unit in place. */
+/* Whole-iteration fusion for small units: a wide BF16 unit with m <= 128
+ * (e.g. the 128 x n heads of per-head Muon, RFC section 4D) can run every
+ * iteration in one launch, one workgroup per unit holding A and B (and, for
+ * MUON_NS_GRAM, the m x m iterates) in on-chip memory.  The quintic
+ * accumulates the next iteration's Gram product while the update is stored,
+ * so the iterate is read once and written once per iteration; the Gram form
+ * reads the input twice and writes the result once in all.  Results are
+ * bit-identical to the unfused kernels.  AUTO fuses when the call has at
+ * least as many units as the device has compute units (every CU gets a
+ * unit); ON whenever eligible; OFF never.  Not eligible: tall units,
+ * m > 128, F32 compute, and outputs that overlap an input other than their
+ * own (in place, unit for unit, is fine). */
 typedef enum { MUON_FUSE_AUTO = 0, MUON_FUSE_OFF = 1, MUON_FUSE_ON = 2 } muon_fuse_t;
 
 /* Newton-Schulz parameters.  The quintic iteration is the one the DeepSpeed

@@ -488,6 +488,33 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   // 2 m <= n, where its error stays at the quintic's level.
   const bool gram_form =
       prm->method == MUON_NS_GRAM && (prm->compute == MUON_F32 || 2 * m <= n);
+  // Small wide units: every iteration in one launch.  A workgroup writes only
+  // its own unit, so an output may be its own input but may not touch any
+  // other matrix's input.
+  const bool small_ok = mfma && !tall && m <= 128 && prm->fuse != MUON_FUSE_OFF &&
+                        (!alias || !cross_overlap(mats, outp, count, unit_bytes * per));
+  if (small_ok && (prm->fuse == MUON_FUSE_ON || L.units >= c->cus)) {
+    NsSmallArgs fa{};
+    fa.src = in.ref;
+    fa.dst = ot.ref;
+    fa.xa = XA;
+    fa.xb = XB;
+    fa.m = static_cast<int>(m);
+    fa.n = static_cast<int>(n);
+    fa.steps = prm->steps;
+    fa.gram = gram_form ? 1 : 0;
+    fa.units = L.units;
+    fa.scale = scale;
+    fa.zflag = zflag;
+    fa.ca = prm->a;
+    fa.cb = prm->b;
+    fa.cc = prm->c;
+    const long k = tstart(c, s, MUON_K_FUSED);
+    e = launch_ns_small(s, fa);
+    tstop(c, s, k);
+    return e == hipSuccess ? MUON_OK : hip_fail(c, e, "fused launch");
+  }
+
   if (gram_form) {
     // m x m matrices live in A, B and (at m x m stride) the two iterate
     // regions; the input is read by the first and the last product only.
@@ -561,32 +588,6 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
       if (e != hipSuccess) return hip_fail(c, e, "copy launch");
     }
     return MUON_OK;
-  }
-
-  // Small wide units: every iteration in one launch.  A workgroup writes only
-  // its own unit, so an output may be its own input but may not touch any
-  // other matrix's input.
-  const bool small_ok = mfma && !tall && m <= 128 && prm->fuse != MUON_FUSE_OFF &&
-                        (!alias || !cross_overlap(mats, outp, count, unit_bytes * per));
-  if (small_ok && (prm->fuse == MUON_FUSE_ON || L.units >= c->cus)) {
-    NsSmallArgs fa{};
-    fa.src = in.ref;
-    fa.dst = ot.ref;
-    fa.xa = XA;
-    fa.xb = XB;
-    fa.m = static_cast<int>(m);
-    fa.n = static_cast<int>(n);
-    fa.steps = prm->steps;
-    fa.units = L.units;
-    fa.scale = scale;
-    fa.zflag = zflag;
-    fa.ca = prm->a;
-    fa.cb = prm->b;
-    fa.cc = prm->c;
-    const long k = tstart(c, s, MUON_K_FUSED);
-    e = launch_ns_small(s, fa);
-    tstop(c, s, k);
-    return e == hipSuccess ? MUON_OK : hip_fail(c, e, "fused launch");
   }
 
   for (int k = 0; k < prm->steps; ++k) {

@@ -45,12 +45,14 @@ struct NsNormArgs {
   float eps;
 };
 
-// The whole quintic iteration of wide units with m <= 128 in one launch
-// (ns_small.hip): src = the units Y (m x n, rows contiguous), dst = the
-// result, xa / xb = two iterate regions of m x n per unit.
+// The whole iteration (quintic, or its Gram form) of wide units with
+// m <= 128 in one launch (ns_small.hip): src = the units Y (m x n, rows
+// contiguous), dst = the result, xa / xb = two iterate regions of m x n per
+// unit (quintic only).
 struct NsSmallArgs {
   MatRef src, dst, xa, xb;
   int m, n, steps;
+  int gram;            // 1: Gram form (m x m iteration, then X = s Q Y)
   int64_t units;
   const float* scale;  // per-unit s = 1 / (||Y||_F + eps)
   const int* zflag;    // per-unit "norm is zero" flag, or nullptr

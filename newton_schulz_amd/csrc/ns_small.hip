@@ -109,6 +109,7 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+template <bool GRAM>
 __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
   __shared__ __attribute__((aligned(1024))) char bp[2 * HALF];  // B'
   __shared__ __attribute__((aligned(1024))) char am[2 * HALF];  // A; the X' block staging
@@ -203,44 +204,55 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     barrier_lds();
   }
 
-  for (int k = 0; k < a.steps; ++k) {
-    const bool last = k + 1 == a.steps;
-    // ---- B' = a I + b A + c A A
-    {
-      Acc acc;
-      acc.zero();
+  // C = X Y^T over K = 128 for two K-contiguous 128 x 128 tiles in LDS
+  auto product = [&](const char* x, const char* yy, Acc& acc) {
+    acc.zero();
 #pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        bf16x8_t fa[2], fb[2];
+    for (int kk = 0; kk < 8; ++kk) {
+      bf16x8_t fa[2], fb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          fa[i] = rt_frag(am, wn * 64 + i * 32, kk, lane);
-          fb[i] = rt_frag(am, wm * 64 + i * 32, kk, lane);
-        }
-        acc.mma(fa, fb);
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = rt_frag(yy, wn * 64 + i * 32, kk, lane);
+        fb[i] = rt_frag(x, wm * 64 + i * 32, kk, lane);
       }
-      for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
-        const uint2 w = *reinterpret_cast<const uint2*>(rt_at(am, i, j));
-        const float e[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
-                            __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = a.cb * e[q] + a.cc * acc.v[mi][ni][4 * g + q];
-          if (i == j + q) v[q] += a.ca;
-        }
-        *reinterpret_cast<uint2*>(rt_at(bp, i, j)) = pack4(v);
-      });
-      barrier_lds();
-      mirror_lower(bp, tid);
-      barrier_lds();
+      acc.mma(fa, fb);
     }
-
-    // ---- X_{k+1} = f B' X_k block by block, A_{k+1} accumulated on the way
-    const bf16_t* xs = k == 0 ? y : uniform_ptr(reinterpret_cast<const bf16_t*>(
-                                        mat_at(((k - 1) & 1) ? a.xb : a.xa, u)));
-    const bf16_t* xd = last ? out : uniform_ptr(reinterpret_cast<const bf16_t*>(
-                                        mat_at((k & 1) ? a.xb : a.xa, u)));
+  };
+  // f acc rounded to bf16 into d, then the lower triangle from the upper one
+  auto store_sym = [&](const Acc& acc, char* d, float f) {
+    for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = f * acc.v[mi][ni][4 * g + q];
+      *reinterpret_cast<uint2*>(rt_at(d, i, j)) = pack4(v);
+    });
+    barrier_lds();
+    mirror_lower(d, tid);
+    barrier_lds();
+  };
+  // d = a I + b A + c A A (A in am)
+  auto symsq = [&](char* d) {
+    Acc acc;
+    product(am, am, acc);
+    for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
+      const uint2 w = *reinterpret_cast<const uint2*>(rt_at(am, i, j));
+      const float e[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+                          __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+      float v[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = a.cb * e[q] + a.cc * acc.v[mi][ni][4 * g + q];
+        if (i == j + q) v[q] += a.ca;
+      }
+      *reinterpret_cast<uint2*>(rt_at(d, i, j)) = pack4(v);
+    });
+    barrier_lds();
+    mirror_lower(d, tid);
+    barrier_lds();
+  };
+  // xd = f B xs (B in bp) block by block through the staging tile am; with
+  // `next`, an accumulates xd xd^T from the stored bf16 blocks
+  auto column_pass = [&](const bf16_t* xs, const bf16_t* xd, float f, bool next, Acc& an) {
     const u32x4_t rs = rsrc_words(xs, ubytes);
     uint32_t base[NGC];
     int cc[NGC];
@@ -257,8 +269,6 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
         dma16_asm(rs, sl + (wave + NWV * q) * 1024, c0 + cc[q] < n ? base[q] : kOOB,
                   static_cast<uint32_t>(c0 * 2));
     };
-    const float f = k == 0 ? s : 1.0f;
-    Acc an;  // A_{k+1}
     an.zero();
     issue(s0, 0);
     issue(s1, SM);
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       });
       barrier_lds();
       store_block(xd, c * SM, am);
-      if (!last) {
+      if (next) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
           bf16x8_t fa[2], fb[2];
@@ -308,19 +318,57 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       barrier_lds();  // block c's buffer and the staging are free again
       issue(sl, (c + 3) * SM);
     }
-    // the next iteration reads what this one stored
+    // whatever reads this pass's output next sees every store
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (!last) {
-      for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = an.v[mi][ni][4 * g + q];
-        *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
-      });
-      barrier_lds();
-      mirror_lower(am, tid);
-      barrier_lds();
+  };
+
+  if constexpr (!GRAM) {
+    for (int k = 0; k < a.steps; ++k) {
+      const bool last = k + 1 == a.steps;
+      symsq(bp);  // B'
+      const bf16_t* xs = k == 0 ? y : uniform_ptr(reinterpret_cast<const bf16_t*>(
+                                          mat_at(((k - 1) & 1) ? a.xb : a.xa, u)));
+      const bf16_t* xd = last ? out : uniform_ptr(reinterpret_cast<const bf16_t*>(
+                                          mat_at((k & 1) ? a.xb : a.xa, u)));
+      Acc an;  // A_{k+1}
+      column_pass(xs, xd, k == 0 ? s : 1.0f, !last, an);
+      if (!last) store_sym(an, am, 1.0f);
     }
+  } else {
+    // Gram form: P_k = a I + b A_k + c A_k^2, Q_{k+1} = P_k Q_k (Q_1 = P_0),
+    // A_{k+1} = (P_k A_k) P_k, all m x m in LDS (A in am, P in bp, Q and a
+    // scratch product in the free slab buffers); then X = s Q Y.
+    char* q = s1;
+    char* t = s0;
+    for (int k = 0; k < a.steps; ++k) {
+      char* p = k == 0 ? q : bp;
+      symsq(p);
+      if (k > 0) {
+        Acc c;
+        product(p, q, c);
+        store_sym(c, t, 1.0f);
+        char* w = q;
+        q = t;
+        t = w;
+      }
+      if (k + 1 < a.steps) {
+        Acc c;
+        product(p, am, c);
+        store_sym(c, t, 1.0f);
+        Acc c2;
+        product(t, p, c2);
+        store_sym(c2, am, 1.0f);
+      }
+    }
+    // Q into bp, the slab buffers carry the input blocks
+#pragma unroll
+    for (int it = 0; it < 2 * HALF / 16 / (64 * NWV); ++it) {
+      const int e = 16 * (tid + 64 * NWV * it);
+      *reinterpret_cast<u32x4_t*>(bp + e) = *reinterpret_cast<const u32x4_t*>(q + e);
+    }
+    barrier_lds();
+    Acc unused;
+    column_pass(y, out, s, false, unused);
   }
 }
 
@@ -331,6 +379,9 @@ hipError_t launch_ns_small(hipStream_t s, const NsSmallArgs& a) {
   if (a.m < 1 || a.m > SM || a.n < a.m || a.m % 8 || a.n % 8 || a.steps < 1 ||
       static_cast<int64_t>(a.m) * a.n * 2 >= (int64_t{1} << 31) || a.units > 0x7fffffff)
     return hipErrorInvalidValue;
-  ns_small_kernel<<<static_cast<unsigned>(a.units), 64 * NWV, 0, s>>>(a);
+  if (a.gram)
+    ns_small_kernel<true><<<static_cast<unsigned>(a.units), 64 * NWV, 0, s>>>(a);
+  else
+    ns_small_kernel<false><<<static_cast<unsigned>(a.units), 64 * NWV, 0, s>>>(a);
   return hipGetLastError();
 }

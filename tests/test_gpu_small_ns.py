@@ -1,10 +1,11 @@
 """The fused whole-iteration Newton-Schulz of small wide units (m <= 128).
 
-It computes the quintic iteration with the unfused kernels' rounding points,
-MFMA shape and summation order, so its output must equal theirs bit for bit
-(fuse "on" against fuse "off" on the same inputs); against the CPU oracle the
-bf16 bar holds (relative Frobenius error per unit <= 2e-2).  Eligibility and
-the automatic choice are checked through the per-class launch counts.
+It computes the quintic iteration, or its Gram form, with the unfused
+kernels' rounding points, MFMA shape and summation order, so its output must
+equal theirs bit for bit (fuse "on" against fuse "off" on the same inputs);
+against the CPU oracle the bf16 bar holds (relative Frobenius error per unit
+<= 2e-2).  Eligibility and the automatic choice are checked through the
+per-class launch counts.
 """
 import sys
 
@@ -54,12 +55,14 @@ def launches(ctx, fn):
     return t["fused"][1], t["update"][1]
 
 
-def both(ctx, mats, head_rows=0, steps=5):
+def both(ctx, mats, head_rows=0, steps=5, method="quintic"):
     a = [torch.empty_like(m) for m in mats]
     b = [torch.empty_like(m) for m in mats]
-    nf, _ = launches(ctx, lambda: ctx.newton_schulz(mats, a, head_rows, ns_params(steps=steps, fuse="on")))
-    nu, upd = launches(ctx, lambda: ctx.newton_schulz(mats, b, head_rows, ns_params(steps=steps, fuse="off")))
-    assert nf == 1 and nu == 0 and upd == steps, (nf, nu, upd)
+    nf, _ = launches(ctx, lambda: ctx.newton_schulz(mats, a, head_rows,
+                                                    ns_params(steps=steps, method=method, fuse="on")))
+    nu, upd = launches(ctx, lambda: ctx.newton_schulz(mats, b, head_rows,
+                                                      ns_params(steps=steps, method=method, fuse="off")))
+    assert nf == 1 and nu == 0 and upd == (steps if method == "quintic" else 1), (nf, nu, upd)
     return a, b
 
 
@@ -143,9 +146,42 @@ def test_fused_irregular_placement_and_zero_units(ctx):
         assert torch.equal(x, y)
 
 
+# the Gram form (bf16: units with 2 m <= n) fuses as well
+@pytest.mark.parametrize("rows,cols,count", [(128, 2560, 3), (64, 512, 2), (128, 256, 2), (96, 4096, 1),
+                                             (8, 64, 2), (120, 1000, 2)])
+def test_fused_gram_form_equals_unfused_and_oracle(ctx, rows, cols, count):
+    g = gen(rows * 17 + cols)
+    mats = [synth.normal((rows, cols), 1e-3, g, DEV, torch.bfloat16) for _ in range(count)]
+    a, b = both(ctx, mats, method="gram")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    worst = check_oracle(mats, a)
+    say(f"  fused gram form {rows}x{cols} x{count}: bit-identical to unfused; max rel err {worst:.3e}")
+    assert worst <= BF16_TOL
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 6])
+def test_fused_gram_form_step_counts_and_in_place(ctx, steps):
+    g = gen(200 + steps)
+    h = 128
+    mats = [synth.normal((3 * h, 1024), 1e-3, g, DEV, torch.bfloat16) for _ in range(2)]
+    mats[1][h:2 * h].zero_()  # one zero head
+    a, b = both(ctx, mats, head_rows=h, steps=steps, method="gram")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert not torch.any(a[1][h:2 * h])
+    assert check_oracle(mats, a, head_rows=h, steps=steps) <= BF16_TOL
+    ip = [m.clone() for m in mats]
+    nf, _ = launches(ctx, lambda: ctx.newton_schulz(ip, None, h, ns_params(steps=steps, method="gram",
+                                                                            fuse="on")))
+    assert nf == 1
+    for x, y in zip(a, ip):
+        assert torch.equal(x, y)
+
+
 def test_fused_eligibility(ctx):
     g = gen(13)
-    # tall units, m > 128, fp32 compute and the Gram form are never fused
+    # tall units, m > 128 and fp32 compute are never fused
     tall = [synth.normal((256, 64), 1e-3, g, DEV, torch.bfloat16) for _ in range(2)]
     nf, _ = launches(ctx, lambda: ctx.newton_schulz(tall, [torch.empty_like(t) for t in tall], 0,
                                                     ns_params(fuse="on")))
@@ -158,10 +194,16 @@ def test_fused_eligibility(ctx):
     nf, _ = launches(ctx, lambda: ctx.newton_schulz(f32, [torch.empty_like(t) for t in f32], 0,
                                                     ns_params(compute="f32", fuse="on")))
     assert nf == 0
-    small = [synth.normal((128, 512), 1e-3, g, DEV, torch.bfloat16) for _ in range(2)]
-    nf, _ = launches(ctx, lambda: ctx.newton_schulz(small, [torch.empty_like(t) for t in small], 0,
-                                                    ns_params(method="gram", fuse="on")))
-    assert nf == 0
+    # the Gram form on a near-square unit runs the quintic (bf16: 2 m > n), fused
+    sq = [synth.normal((128, 200), 1e-3, g, DEV, torch.bfloat16) for _ in range(2)]
+    o1 = [torch.empty_like(t) for t in sq]
+    o2 = [torch.empty_like(t) for t in sq]
+    nf, _ = launches(ctx, lambda: ctx.newton_schulz(sq, o1, 0, ns_params(method="gram", fuse="on")))
+    assert nf == 1
+    ctx.newton_schulz(sq, o2, 0, ns_params(fuse="off"))
+    torch.cuda.synchronize()
+    for x, y in zip(o1, o2):
+        assert torch.equal(x, y)
     # an output that overlaps another unit's input is not fused (and is right)
     buf = synth.normal((3 * 128 * 512,), 1e-3, g, DEV, torch.bfloat16)
     ins = [buf[i * 128 * 512:(i + 1) * 128 * 512].view(128, 512) for i in range(2)]
