@@ -35,12 +35,18 @@ nor the momentum formula; the readings taken here are:
     splitting fused tensors into their logical matrices).
   * apply (binary32): eta = lr*scale; W1 = W*(1 - lr*wd) when wd != 0;
     W' = W1 - eta*u; optional bf16 copy of W' rounded to nearest-even.
+  * per-iteration coefficients (RFC section 5, "Polar Express", named but
+    not given): each iteration's quintic is the best one, in the maximum
+    norm, on the interval that holds the singular values at that point
+    (`minimax_schedule`, whose comment block lists the readings).
 
 Pins (tests/test_oracle_*.py, run without a GPU) tie each function to facts
 other than itself: the SVD closed form of the odd matrix polynomial, diagonal
 and rank-1 inputs, transpose / sign / scale / orthogonal symmetries, an
 independent Gram-recursion evaluation, exact rational emulation of the
-binary32 momentum and apply sequences, and torch's CPU bfloat16 cast.
+binary32 momentum and apply sequences, torch's CPU bfloat16 cast, and for the
+per-iteration coefficients a linear-programme solution of the same best
+approximation, the alternation property and the closed-form limit polynomial.
 """
 from __future__ import annotations
 
@@ -115,7 +121,7 @@ def momentum_ref(g, M, beta: float = 0.95, nesterov: bool = True):
 # Newton-Schulz orthogonalisation, float64.
 # ---------------------------------------------------------------------------
 def ns_ref(Y, steps: int = NS_STEPS, a: float = NS_A, b: float = NS_B,
-           c: float = NS_C, eps: float = NS_EPS) -> np.ndarray:
+           c: float = NS_C, eps: float = NS_EPS, coeffs=None) -> np.ndarray:
     """Quintic Newton-Schulz of one 2D matrix, in float64.
 
     The iteration drives every singular value of the normalised matrix
@@ -123,6 +129,10 @@ def ns_ref(Y, steps: int = NS_STEPS, a: float = NS_A, b: float = NS_B,
     have unit spectral norm; section 5: the quintic iteration).  A tall
     matrix (rows > cols) is processed as its transpose so that the Gram
     matrix is the small side; the result is transposed back.
+
+    `coeffs`: optional per-iteration coefficients, `steps` rows of (a, b, c);
+    iteration k then uses row k instead of the fixed (a, b, c) (RFC section
+    5: per-iteration optimised coefficients, see `minimax_schedule`).
     """
     X = np.array(Y, dtype=np.float64, copy=True)
     if X.ndim != 2:
@@ -131,10 +141,15 @@ def ns_ref(Y, steps: int = NS_STEPS, a: float = NS_A, b: float = NS_B,
     if tall:
         X = X.T
     X = X / (np.linalg.norm(X, "fro") + eps)
-    for _ in range(steps):
+    rows = [(a, b, c)] * steps
+    if coeffs is not None:
+        rows = [tuple(float(v) for v in r) for r in np.asarray(coeffs, dtype=np.float64)]
+        if len(rows) != steps or any(len(r) != 3 for r in rows):
+            raise ValueError("coeffs must hold `steps` rows of (a, b, c)")
+    for ak, bk, ck in rows:
         A = X @ X.T
-        B = b * A + c * (A @ A)
-        X = a * X + B @ X
+        B = bk * A + ck * (A @ A)
+        X = ak * X + B @ X
     if tall:
         X = X.T
     return np.ascontiguousarray(X)
@@ -155,6 +170,102 @@ def ns_ref_heads(Y, head_rows: int = 0, **kw) -> np.ndarray:
     if head_rows <= 0:
         return ns_ref(Y, **kw)
     return np.concatenate([ns_ref(blk, **kw) for blk in split_heads(Y, head_rows)], axis=0)
+
+
+# ---------------------------------------------------------------------------
+# Per-iteration coefficients (DeepSpeed RFC, section 5 Roadmap: Newton-Schulz
+# whose coefficients are optimised for each iteration, "Polar Express", so
+# that fewer iterations reach the same accuracy).  The pages name the idea but
+# give neither a table nor a derivation; the reading taken here:
+#
+#   * iteration t applies p_t(x) = a x + b x^3 + c x^5 to every singular
+#     value, and p_t is the odd quintic closest to 1 in the maximum norm over
+#     the interval [l_t, u_t (1 + margin)] that holds the singular values
+#     (greedy: each step the best one for where the values are now);
+#   * X_0 is normalised by its Frobenius norm, so u_0 = 1; l_0 = `lo` is the
+#     smallest singular value the schedule is built to lift (a parameter);
+#   * the values land in p_t's image [1 - E_t, 1 + E_t], the next interval;
+#   * `margin` widens each interval at the top: above it the polynomial
+#     climbs steeply, and bf16 rounding (2^-8 relative per rounding, a few
+#     per iteration) would otherwise push the top values past it and let
+#     them grow without bound over the later iterations;
+#   * once an interval is narrower than 1e-3 the limit of the best
+#     polynomial as the interval shrinks to {1} is used:
+#     (a, b, c) = (15/8, -5/4, 3/8), which matches 1 to third order at 1 and
+#     is increasing everywhere, p'(x) = (15/8) (1 - x^2)^2.
+# ---------------------------------------------------------------------------
+MINIMAX_LO = 1e-3
+MINIMAX_MARGIN = 0.02
+LIMIT_QUINTIC = (15.0 / 8.0, -10.0 / 8.0, 3.0 / 8.0)
+
+
+def minimax_quintic(lo: float, hi: float, iters: int = 100):
+    """Odd quintic p minimising max over [lo, hi] of |1 - p(x)|, 0 < lo < hi.
+
+    Remez exchange on four reference points.  The error 1 - p of the best p
+    alternates in sign on four points (Chebyshev alternation for the Haar
+    system x, x^3, x^5 on an interval away from 0); p has at most two
+    interior critical points (p' is a quadratic in x^2), so the endpoints are
+    two of them.  Each round solves p(x_i) + s_i E = 1 with s = (+, -, +, -)
+    and moves the two interior points to the new critical points.
+    Returns (a, b, c, E), E = max |1 - p| on [lo, hi].
+    """
+    lo, hi = float(lo), float(hi)
+    if not (0.0 < lo < hi):
+        raise ValueError("need 0 < lo < hi")
+    x = np.array([lo, 0.0, 0.0, hi])
+    x[1:3] = lo + (hi - lo) * (1.0 - np.cos(np.pi * np.array([1.0, 2.0]) / 3.0)) / 2.0
+    sign = np.array([1.0, -1.0, 1.0, -1.0])
+    for _ in range(iters):
+        M = np.stack([x, x ** 3, x ** 5, sign], axis=1)
+        a, b, c, E = np.linalg.solve(M, np.ones(4))
+        disc = 9.0 * b * b - 20.0 * a * c
+        if c == 0.0 or disc < 0.0:
+            raise ArithmeticError("Remez lost the alternation")
+        roots = np.sort([(-3.0 * b - np.sqrt(disc)) / (10.0 * c),
+                         (-3.0 * b + np.sqrt(disc)) / (10.0 * c)])
+        if not (lo * lo < roots[0] < roots[1] < hi * hi):
+            raise ArithmeticError("Remez lost the alternation")
+        xn = np.array([lo, np.sqrt(roots[0]), np.sqrt(roots[1]), hi])
+        done = np.max(np.abs(xn - x)) <= 1e-15 * hi
+        x = xn
+        if done:
+            break
+    M = np.stack([x, x ** 3, x ** 5, sign], axis=1)
+    a, b, c, E = np.linalg.solve(M, np.ones(4))
+    return float(a), float(b), float(c), float(abs(E))
+
+
+def quintic_eval(coef, x):
+    """p(x) = a x + b x^3 + c x^5."""
+    a, b, c = coef
+    x = np.asarray(x, dtype=np.float64)
+    return a * x + b * x ** 3 + c * x ** 5
+
+
+def minimax_schedule(steps: int, lo: float = MINIMAX_LO, margin: float = MINIMAX_MARGIN):
+    """Per-iteration (a, b, c) rows (steps x 3, float64) and the final bound.
+
+    Returns (rows, E): every singular value of X_0 in [lo, 1] ends, in exact
+    arithmetic, within [1 - E, 1 + E] after the `steps` iterations.
+    """
+    if steps < 1 or not (0.0 < lo < 1.0) or not (0.0 <= margin <= 0.5):
+        raise ValueError("steps >= 1, 0 < lo < 1, 0 <= margin <= 0.5")
+    l, u = float(lo), 1.0
+    rows = []
+    E = 1.0 - l
+    for _ in range(steps):
+        top = u * (1.0 + margin)
+        if top - l < 1e-3:
+            coef = LIMIT_QUINTIC
+            # increasing everywhere: the extremes sit at the ends
+            E = max(1.0 - float(quintic_eval(coef, l)), float(quintic_eval(coef, top)) - 1.0)
+        else:
+            a, b, c, E = minimax_quintic(l, top)
+            coef = (a, b, c)
+        rows.append(coef)
+        l, u = 1.0 - E, 1.0 + E
+    return np.array(rows, dtype=np.float64), float(E)
 
 
 # ---------------------------------------------------------------------------
