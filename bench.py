@@ -17,6 +17,7 @@ the Gram form instead; `value` then still counts the quintic's flops
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -96,9 +97,10 @@ def traffic_record(*kernel_src: str):
     return round(rec.get("hbm_bytes_per_launch"))
 
 
-def cpu_baseline(seconds_budget: float = 20.0):
+def cpu_baseline(seconds_budget: float = 20.0, ns_steps: int = 5, minimax: bool = False):
     """The oracle (numpy fp64 Newton-Schulz, binary32 momentum/apply) on one
-    Qwen3-4B layer, timed on this host's cores."""
+    Qwen3-4B layer, timed on this host's cores, with the same iteration count
+    and coefficients as the timed GPU run."""
     import numpy as np
     import oracle
     from newton_schulz_amd import synth
@@ -111,6 +113,9 @@ def cpu_baseline(seconds_budget: float = 20.0):
     w = synth.qwen3_4b_layer()
     rng = np.random.default_rng(0)
     mats = [(m.rows, m.cols) for m in w.mats]
+    ns_kw = {"steps": ns_steps}
+    if minimax:
+        ns_kw["coeffs"] = oracle.minimax_schedule(ns_steps)[0]
     t_ns = t_el = 0.0
     flops = 0
     done = 0
@@ -122,13 +127,13 @@ def cpu_baseline(seconds_budget: float = 20.0):
             t0 = time.perf_counter()
             M, U = oracle.momentum_ref(g, M, 0.95, True)
             t1 = time.perf_counter()
-            O = oracle.ns_ref(oracle.bf16_round(U))
+            O = oracle.ns_ref(oracle.bf16_round(U), **ns_kw)
             t2 = time.perf_counter()
             oracle.apply_ref(W, oracle.bf16_round(O.astype(np.float32)), 0.02, bf16_copy=True)
             t3 = time.perf_counter()
             t_el += (t1 - t0) + (t3 - t2)
             t_ns += t2 - t1
-            flops += sum(ns_flops(min(r, c), max(r, c)))
+            flops += sum(ns_flops(min(r, c), max(r, c), ns_steps))
             done += 1
             if t_ns + t_el > seconds_budget:
                 break
@@ -162,6 +167,10 @@ def main():
     ap.add_argument("--workload", default="qwen3_4b")
     ap.add_argument("--ns-method", default="quintic", choices=["quintic", "gram"],
                     help="Newton-Schulz evaluation; value stays the quintic's flops / step time")
+    ap.add_argument("--ns-coeffs", default="fixed", choices=["fixed", "minimax"],
+                    help="fixed quintic (a, b, c), or the per-iteration minimax schedule")
+    ap.add_argument("--ns-steps", type=int, default=0,
+                    help="Newton-Schulz iterations (default: the workload's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip per-kernel event timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -186,11 +195,14 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}), flush=True)
         return
     w = workload_by_name(args.workload)
+    if args.ns_steps:
+        w = dataclasses.replace(w, ns_steps=args.ns_steps)
     shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
     keep_bf16 = not args.workload.startswith("qwen3_30b_experts")
     ms = MuonStep(shapes, dev, lr=w.lr, beta=w.beta, nesterov=w.nesterov, compute=w.compute,
                   grad_dtype=w.grad_dtype, cap_bytes=w.cap_bytes, cap_kind=w.cap_kind,
-                  ns_steps=w.ns_steps, keep_bf16_weights=keep_bf16, ns_method=args.ns_method)
+                  ns_steps=w.ns_steps, keep_bf16_weights=keep_bf16, ns_method=args.ns_method,
+                  ns_coeffs=None if args.ns_coeffs == "fixed" else args.ns_coeffs)
     g = torch.Generator(device=dev).manual_seed(w.seed)
     for i, W0 in enumerate(synth.draw_weights(w, g, dev)):
         ms.view(ms.master, i).copy_(W0)
@@ -305,6 +317,7 @@ def main():
         "data": "synthetic (seeded N(0,1e-3) bf16 gradients, fp32 state; no checkpoint)",
         "config": {"workload": w.name, "matrices": len(w.mats), "muon_params": numel,
                    "ns_units": len(units), "ns_steps": w.ns_steps, "ns_method": args.ns_method,
+                   "ns_coeffs": args.ns_coeffs,
                    "micro_bucket_cap_bytes": w.cap_bytes, "cap_kind": w.cap_kind,
                    "micro_buckets": len(ms.plan.buckets), "workspace_bytes": ms.plan.max_workspace,
                    "parallelism": "single GPU"},
@@ -318,7 +331,7 @@ def main():
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline"] = cpu_baseline(ns_steps=w.ns_steps, minimax=args.ns_coeffs == "minimax")
     print(json.dumps(out), flush=True)
 
 

@@ -71,9 +71,11 @@ typedef enum { MUON_NS_QUINTIC = 0, MUON_NS_GRAM = 1 } muon_ns_method_t;
  * bit-identical to the unfused kernels.  AUTO fuses when the call has at
  * least as many units as the device has compute units (every CU gets a
  * unit); ON whenever eligible; OFF never.  Not eligible: tall units,
- * m > 128, F32 compute, and outputs that overlap an input other than their
- * own (in place, unit for unit, is fine). */
+ * m > 128, F32 compute, a per-iteration coefficient table of more than
+ * MUON_NS_FUSED_MAX_ROWS rows, and outputs that overlap an input other than
+ * their own (in place, unit for unit, is fine). */
 typedef enum { MUON_FUSE_AUTO = 0, MUON_FUSE_OFF = 1, MUON_FUSE_ON = 2 } muon_fuse_t;
+#define MUON_NS_FUSED_MAX_ROWS 16
 
 /* Newton-Schulz parameters.  The quintic iteration is the one the DeepSpeed
  * RFC "Enable Correct and High-Performance Muon Optimizer under ZeRO CPU
@@ -85,7 +87,14 @@ typedef enum { MUON_FUSE_AUTO = 0, MUON_FUSE_OFF = 1, MUON_FUSE_ON = 2 } muon_fu
  * with one operand fewer).
  * X_0 = Y / (||Y||_F + eps); a tall Y (rows > cols) is processed as Y^T and
  * the result transposed back.  Defaults (muon_ns_params_default):
- * steps 5, (a, b, c) = (3.4445, -4.7750, 2.0315), eps 1e-7, compute BF16. */
+ * steps 5, (a, b, c) = (3.4445, -4.7750, 2.0315), eps 1e-7, compute BF16,
+ * coeffs NULL.
+ * Per-iteration coefficients (RFC section 5, Roadmap: coefficients optimised
+ * for each iteration, "Polar Express"): when coeffs is not NULL it points to
+ * `steps` rows of three floats (a_k, b_k, c_k), row-major, in HOST memory,
+ * read during the call only; iteration k uses row k in place of (a, b, c)
+ * (Gram form: P_k = a_k I + b_k A_k + c_k A_k^2).  Every value must be
+ * finite.  muon_ns_minimax_coeffs fills such a table. */
 typedef struct {
   int32_t steps;     /* >= 0 */
   float a, b, c;     /* quintic coefficients */
@@ -94,6 +103,7 @@ typedef struct {
                         F32 = fp32 verification mode */
   int32_t method;    /* muon_ns_method_t, default MUON_NS_QUINTIC */
   int32_t fuse;      /* muon_fuse_t, default MUON_FUSE_AUTO */
+  const float* coeffs; /* NULL, or steps x 3 per-iteration (a, b, c), host */
 } muon_ns_params_t;
 
 /* Geometry of one weight matrix (RFC section 4A: keep the 2D shape and head
@@ -130,6 +140,27 @@ size_t muon_ctx_workspace_bytes(const muon_ctx_t* ctx);
 
 /* Fill *p with the defaults listed above. */
 void muon_ns_params_default(muon_ns_params_t* p);
+
+/* Per-iteration coefficients (RFC section 5, Roadmap: Newton-Schulz with
+ * coefficients optimised per iteration, so that fewer iterations reach the
+ * same accuracy; the page gives no table).  Iteration t maps each singular
+ * value x to p_t(x) = a x + b x^3 + c x^5, where p_t is the odd quintic with
+ * the smallest max |1 - p(x)| over [l_t, u_t (1 + margin)], the interval
+ * that holds the singular values at that point; l_0 = lo, u_0 = 1 (X_0 is
+ * normalised by its Frobenius norm), and the next interval is p_t's image
+ * [1 - E_t, 1 + E_t], E_t the attained maximum.  `margin` widens each
+ * interval at the top, where p_t climbs steeply, so that values that bf16
+ * rounding pushes slightly past it stay bounded and rounding errors near
+ * the top are amplified less (0.05 is the binding's default: a few bf16
+ * roundings of 2^-8 each, with room).  An interval narrower than 1e-3 takes the limit
+ * polynomial (15/8, -5/4, 3/8).  Pure host function, computed in double.
+ * out: `steps` x 3 floats (caller-owned, host).  *bound (may be NULL)
+ * receives E_{steps-1}: in exact arithmetic every singular value of X_0 in
+ * [lo, 1] ends within [1 - bound, 1 + bound].  Errors: MUON_EINVAL (steps < 1
+ * or > 1024, lo outside (0, 1), margin outside [0, 0.5], out NULL, or the
+ * exchange did not converge). */
+muon_status_t muon_ns_minimax_coeffs(int32_t steps, double lo, double margin, float* out,
+                                     double* bound);
 
 /* Workspace one muon_newton_schulz_batched call needs for `count` matrices
  * of `shape` in compute dtype `compute` (pure host function).  Per Newton-

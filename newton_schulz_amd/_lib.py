@@ -15,6 +15,7 @@ KERNEL_CLASSES = ["momentum", "norm", "gram", "symsq", "update", "apply", "prod"
 # every symbol include/muon.h declares
 EXPORTS = [
     "muon_create", "muon_destroy", "muon_ctx_workspace_bytes", "muon_ns_params_default",
+    "muon_ns_minimax_coeffs",
     "muon_ns_workspace_bytes", "muon_plan_create", "muon_plan_num_buckets", "muon_plan_bucket",
     "muon_plan_max_workspace", "muon_plan_destroy", "muon_momentum_update",
     "muon_newton_schulz_batched", "muon_apply", "muon_status_string", "muon_last_error",
@@ -25,7 +26,8 @@ EXPORTS = [
 class NsParams(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
                 ("c", ctypes.c_float), ("eps", ctypes.c_float), ("compute", ctypes.c_int32),
-                ("method", ctypes.c_int32), ("fuse", ctypes.c_int32)]
+                ("method", ctypes.c_int32), ("fuse", ctypes.c_int32),
+                ("coeffs", ctypes.POINTER(ctypes.c_float))]
 
 
 class Shape(ctypes.Structure):
@@ -59,6 +61,8 @@ def load() -> ctypes.CDLL:
         "muon_destroy": (i32, [vp]),
         "muon_ctx_workspace_bytes": (sz, [vp]),
         "muon_ns_params_default": (None, [P(NsParams)]),
+        "muon_ns_minimax_coeffs": (i32, [i32, ctypes.c_double, ctypes.c_double, P(f32),
+                                         P(ctypes.c_double)]),
         "muon_ns_workspace_bytes": (sz, [Shape, i64, i32]),
         "muon_plan_create": (i32, [P(Shape), i64, sz, i32, i32, i32, P(vp)]),
         "muon_plan_num_buckets": (i64, [vp]),

@@ -50,11 +50,39 @@ NS_FUSE = {"auto": 0, "off": 1, "on": 2}
 NS_METHODS = {"quintic": 0, "gram": 1}
 
 
+def minimax_coeffs(steps: int, lo: float = 1e-3, margin: float = 0.05) -> Tuple[list, float]:
+    """Per-iteration (a, b, c) rows from libmuon's muon_ns_minimax_coeffs and
+    the bound E after the last one (every singular value of X_0 in [lo, 1]
+    ends in [1 - E, 1 + E] in exact arithmetic)."""
+    lib = _lib.load()
+    out = (ctypes.c_float * (3 * steps))()
+    bound = ctypes.c_double()
+    st = lib.muon_ns_minimax_coeffs(steps, lo, margin, out, ctypes.byref(bound))
+    if st != _lib.MUON_OK:
+        raise MuonError(st, "muon_ns_minimax_coeffs")
+    return [tuple(out[3 * k:3 * k + 3]) for k in range(steps)], bound.value
+
+
 def ns_params(steps: int = 5, a: float = 3.4445, b: float = -4.7750, c: float = 2.0315,
               eps: float = 1e-7, compute: str = "bf16", method: str = "quintic",
-              fuse: str = "auto") -> NsParams:
-    return NsParams(steps, a, b, c, eps, MUON_BF16 if compute == "bf16" else MUON_F32,
-                    NS_METHODS[method], NS_FUSE[fuse])
+              fuse: str = "auto", coeffs=None, lo: float = 1e-3,
+              margin: float = 0.05) -> NsParams:
+    """Newton-Schulz parameters.  coeffs: None (the fixed a, b, c), "minimax"
+    (libmuon's per-iteration schedule for `lo`, `margin`), or `steps` rows of
+    (a, b, c).  The returned structure keeps its coefficient table alive."""
+    p = NsParams(steps, a, b, c, eps, MUON_BF16 if compute == "bf16" else MUON_F32,
+                 NS_METHODS[method], NS_FUSE[fuse], None)
+    if coeffs is not None:
+        if isinstance(coeffs, str) and coeffs != "minimax":
+            raise ValueError(f"unknown coefficient schedule {coeffs!r}")
+        rows = minimax_coeffs(steps, lo, margin)[0] if isinstance(coeffs, str) else coeffs
+        flat = [float(v) for r in rows for v in r]
+        if len(flat) != 3 * steps:
+            raise ValueError("coeffs must hold `steps` rows of (a, b, c)")
+        table = (ctypes.c_float * len(flat))(*flat)
+        p.coeffs = ctypes.cast(table, ctypes.POINTER(ctypes.c_float))
+        p._table = table  # owned by the structure for as long as it lives
+    return p
 
 
 def ns_workspace_bytes(rows: int, cols: int, count: int, head_rows: int = 0,

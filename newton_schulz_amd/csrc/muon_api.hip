@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <new>
@@ -139,6 +140,7 @@ void muon_ns_params_default(muon_ns_params_t* p) {
   p->compute = MUON_BF16;
   p->method = MUON_NS_QUINTIC;
   p->fuse = MUON_FUSE_AUTO;
+  p->coeffs = nullptr;
 }
 
 size_t muon_ctx_workspace_bytes(const muon_ctx_t* ctx) { return ctx ? ctx->ws_bytes : 0; }
@@ -351,6 +353,9 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     return fail(c, MUON_EINVAL, "method");
   if (prm->fuse != MUON_FUSE_AUTO && prm->fuse != MUON_FUSE_OFF && prm->fuse != MUON_FUSE_ON)
     return fail(c, MUON_EINVAL, "fuse");
+  if (prm->coeffs != nullptr)
+    for (int64_t k = 0; k < 3 * static_cast<int64_t>(prm->steps); ++k)
+      if (!std::isfinite(prm->coeffs[k])) return fail(c, MUON_EINVAL, "coefficients not finite");
   NsLayout L;
   if (!ns_layout(shape, count, prm->compute, &L)) return fail(c, MUON_ESHAPE, "shape");
   if (count == 0) return MUON_OK;
@@ -429,9 +434,14 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     a.units = L.units;
     a.cus = c->cus;
     a.zflag = zflag;
-    a.ca = prm->a;
-    a.cb = prm->b;
-    a.cc = prm->c;
+  };
+  // (a, b, c) of iteration k: the per-iteration table's row k, else the fixed
+  // coefficients
+  auto coef = [&](int k, float* ca, float* cb, float* cc) {
+    const float* r = prm->coeffs ? prm->coeffs + 3 * static_cast<int64_t>(k) : nullptr;
+    *ca = r ? r[0] : prm->a;
+    *cb = r ? r[1] : prm->b;
+    *cc = r ? r[2] : prm->c;
   };
 
   // Deterministic norm, then per iteration Gram -> symmetric square ->
@@ -492,6 +502,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   // its own unit, so an output may be its own input but may not touch any
   // other matrix's input.
   const bool small_ok = mfma && !tall && m <= 128 && prm->fuse != MUON_FUSE_OFF &&
+                        (prm->coeffs == nullptr || prm->steps <= MUON_NS_FUSED_MAX_ROWS) &&
                         (!alias || !cross_overlap(mats, outp, count, unit_bytes * per));
   if (small_ok && (prm->fuse == MUON_FUSE_ON || L.units >= c->cus)) {
     NsSmallArgs fa{};
@@ -506,9 +517,9 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     fa.units = L.units;
     fa.scale = scale;
     fa.zflag = zflag;
-    fa.ca = prm->a;
-    fa.cb = prm->b;
-    fa.cc = prm->c;
+    // a fixed triple is one row that every iteration reuses
+    fa.ncoef = prm->coeffs ? prm->steps : 1;
+    for (int k = 0; k < fa.ncoef; ++k) coef(k, &fa.coef[k][0], &fa.coef[k][1], &fa.coef[k][2]);
     const long k = tstart(c, s, MUON_K_FUSED);
     e = launch_ns_small(s, fa);
     tstop(c, s, k);
@@ -545,6 +556,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
       sa.pm = AR; sa.pn = AR; sa.dst = P; sa.epi = AR;
       sa.ldm = sa.ldn = sa.ldd = sa.lde = m;
       sa.M = sa.N = sa.K = static_cast<int>(m);
+      coef(k, &sa.ca, &sa.cb, &sa.cc);
       e = gemm(MUON_K_SYMSQ, sa, EPI_SYMSQ, false, false);
       if (e != hipSuccess) return hip_fail(c, e, "symsq launch");
       if (k > 0) {
@@ -611,6 +623,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     sa.pm = AR; sa.pn = AR; sa.dst = BR; sa.epi = AR;
     sa.ldm = sa.ldn = sa.ldd = sa.lde = m;
     sa.M = sa.N = sa.K = static_cast<int>(m);
+    coef(k, &sa.ca, &sa.cb, &sa.cc);
     e = gemm(MUON_K_SYMSQ, sa, EPI_SYMSQ, false, false);
     if (e != hipSuccess) return hip_fail(c, e, "symsq launch");
 

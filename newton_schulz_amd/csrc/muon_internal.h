@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "muon.h"
 #include "muon_device.h"
 
 // Epilogue kinds of the Newton-Schulz matrix products.
@@ -56,7 +57,8 @@ struct NsSmallArgs {
   int64_t units;
   const float* scale;  // per-unit s = 1 / (||Y||_F + eps)
   const int* zflag;    // per-unit "norm is zero" flag, or nullptr
-  float ca, cb, cc;    // quintic coefficients a, b, c
+  int ncoef;           // rows of coef: iteration k uses row min(k, ncoef - 1)
+  float coef[MUON_NS_FUSED_MAX_ROWS][3];  // (a, b, c) per iteration
 };
 
 hipError_t launch_ns_small(hipStream_t s, const NsSmallArgs& a);

@@ -230,8 +230,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     mirror_lower(d, tid);
     barrier_lds();
   };
-  // d = a I + b A + c A A (A in am)
-  auto symsq = [&](char* d) {
+  // d = a I + b A + c A A (A in am) with iteration k's coefficients
+  auto symsq = [&](char* d, int k) {
+    const int r = k < a.ncoef ? k : a.ncoef - 1;
+    const float ca = a.coef[r][0], cb = a.coef[r][1], cc = a.coef[r][2];
     Acc acc;
     product(am, am, acc);
     for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
@@ -241,8 +243,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       float v[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        v[q] = a.cb * e[q] + a.cc * acc.v[mi][ni][4 * g + q];
-        if (i == j + q) v[q] += a.ca;
+        v[q] = cb * e[q] + cc * acc.v[mi][ni][4 * g + q];
+        if (i == j + q) v[q] += ca;
       }
       *reinterpret_cast<uint2*>(rt_at(d, i, j)) = pack4(v);
     });
@@ -325,7 +327,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
   if constexpr (!GRAM) {
     for (int k = 0; k < a.steps; ++k) {
       const bool last = k + 1 == a.steps;
-      symsq(bp);  // B'
+      symsq(bp, k);  // B'
       const bf16_t* xs = k == 0 ? y : uniform_ptr(reinterpret_cast<const bf16_t*>(
                                           mat_at(((k - 1) & 1) ? a.xb : a.xa, u)));
       const bf16_t* xd = last ? out : uniform_ptr(reinterpret_cast<const bf16_t*>(
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     char* t = s0;
     for (int k = 0; k < a.steps; ++k) {
       char* p = k == 0 ? q : bp;
-      symsq(p);
+      symsq(p, k);
       if (k > 0) {
         Acc c;
         product(p, q, c);
@@ -377,6 +379,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
 hipError_t launch_ns_small(hipStream_t s, const NsSmallArgs& a) {
   if (a.units <= 0) return hipSuccess;
   if (a.m < 1 || a.m > SM || a.n < a.m || a.m % 8 || a.n % 8 || a.steps < 1 ||
+      a.ncoef < 1 || a.ncoef > MUON_NS_FUSED_MAX_ROWS ||
       static_cast<int64_t>(a.m) * a.n * 2 >= (int64_t{1} << 31) || a.units > 0x7fffffff)
     return hipErrorInvalidValue;
   if (a.gram)

@@ -188,14 +188,16 @@ def ns_ref_heads(Y, head_rows: int = 0, **kw) -> np.ndarray:
 #   * `margin` widens each interval at the top: above it the polynomial
 #     climbs steeply, and bf16 rounding (2^-8 relative per rounding, a few
 #     per iteration) would otherwise push the top values past it and let
-#     them grow without bound over the later iterations;
+#     them grow without bound over the later iterations; near the top the
+#     polynomial is also steep inside the interval, so a wider margin lowers
+#     how much rounding error the later iterations amplify (default 0.05);
 #   * once an interval is narrower than 1e-3 the limit of the best
 #     polynomial as the interval shrinks to {1} is used:
 #     (a, b, c) = (15/8, -5/4, 3/8), which matches 1 to third order at 1 and
 #     is increasing everywhere, p'(x) = (15/8) (1 - x^2)^2.
 # ---------------------------------------------------------------------------
 MINIMAX_LO = 1e-3
-MINIMAX_MARGIN = 0.02
+MINIMAX_MARGIN = 0.05
 LIMIT_QUINTIC = (15.0 / 8.0, -10.0 / 8.0, 3.0 / 8.0)
 
 

@@ -72,7 +72,7 @@ def test_null_context_rejected():
     p = _lib.NsParams()
     lib.muon_ns_params_default(ctypes.byref(p))
     assert (p.steps, round(p.a, 4), round(p.b, 4), round(p.c, 4), p.compute) == (5, 3.4445, -4.775, 2.0315, 1)
-    assert p.method == 0 and p.fuse == 0
+    assert p.method == 0 and p.fuse == 0 and not p.coeffs
     assert lib.muon_momentum_update(None, None, None, 1, None, None, 1, 10, 0.95, 1) == _lib.MUON_EINVAL
     assert lib.muon_apply(None, None, None, None, 1, None, 10, 0.02, 1.0, 0.0) == _lib.MUON_EINVAL
     assert lib.muon_newton_schulz_batched(None, None, None, 1, _lib.Shape(8, 8, 0), 1, ctypes.byref(p),
@@ -199,3 +199,42 @@ def test_plan_rejects_bad_input():
         Plan([(100, 64, 30)], 1 << 20)
     with pytest.raises(MuonError):
         Plan([(0, 64, 0)], 1 << 20)
+
+
+@pytest.mark.parametrize("steps,lo,margin", [
+    (1, 1e-3, 0.02), (6, 1e-3, 0.02), (10, 1e-3, 0.0), (5, 0.1, 0.05), (3, 0.5, 0.0), (8, 1e-4, 0.2),
+])
+def test_minimax_coeffs_match_oracle(steps, lo, margin):
+    """libmuon's host schedule against the oracle's own (independent) one."""
+    import numpy as np
+    import oracle
+    from newton_schulz_amd import minimax_coeffs
+    rows, bound = minimax_coeffs(steps, lo, margin)
+    ref, E = oracle.minimax_schedule(steps, lo, margin)
+    np.testing.assert_allclose(np.array(rows), ref.astype(np.float32), rtol=2e-7, atol=0)
+    assert bound == pytest.approx(E, rel=1e-9, abs=1e-15)
+
+
+def test_minimax_coeffs_rejects_bad_arguments():
+    lib = _lib.load()
+    out = (ctypes.c_float * 30)()
+    ok = lib.muon_ns_minimax_coeffs(10, 1e-3, 0.02, out, None)
+    assert ok == _lib.MUON_OK
+    for steps, lo, margin in [(0, 1e-3, 0.02), (1025, 1e-3, 0.02), (3, 0.0, 0.02), (3, 1.0, 0.02),
+                              (3, float("nan"), 0.02), (3, 1e-3, -0.01), (3, 1e-3, 0.51),
+                              (3, 1e-3, float("nan"))]:
+        assert lib.muon_ns_minimax_coeffs(steps, lo, margin, out, None) == _lib.MUON_EINVAL
+    assert lib.muon_ns_minimax_coeffs(3, 1e-3, 0.02, None, None) == _lib.MUON_EINVAL
+
+
+def test_ns_params_coefficient_table():
+    from newton_schulz_amd import minimax_coeffs, ns_params
+    p = ns_params(steps=4, coeffs="minimax")
+    rows, _ = minimax_coeffs(4)
+    assert [p.coeffs[i] for i in range(12)] == [v for r in rows for v in r]
+    q = ns_params(steps=2, coeffs=[(1.0, 2.0, 3.0), (4.0, 5.0, 6.0)])
+    assert [q.coeffs[i] for i in range(6)] == [1.0, 2.0, 3.0, 4.0, 5.0, 6.0]
+    with pytest.raises(ValueError):
+        ns_params(steps=3, coeffs=[(1.0, 2.0, 3.0)])
+    with pytest.raises(ValueError):
+        ns_params(steps=3, coeffs="chebyshev")
