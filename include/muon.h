@@ -44,6 +44,9 @@ typedef enum {
 
 typedef enum { MUON_F32 = 0, MUON_BF16 = 1 } muon_dtype_t;
 
+/* Elements per sum-of-squares partial (muon_momentum_update_sq). */
+#define MUON_SQ_BLOCK 4096
+
 /* How the iteration is evaluated (the DeepSpeed PR "[Muon] CPU offload: pin
  * the momentum and overlap the host writeback", section Tests, and the RFC's
  * section 5 Roadmap name an ns_method option with a "gram" choice beside the
@@ -104,6 +107,17 @@ typedef struct {
   int32_t method;    /* muon_ns_method_t, default MUON_NS_QUINTIC */
   int32_t fuse;      /* muon_fuse_t, default MUON_FUSE_AUTO */
   const float* coeffs; /* NULL, or steps x 3 per-iteration (a, b, c), host */
+  /* Norms from the momentum pass (see muon_momentum_update_sq): NULL, or the
+   * DEVICE array of sq_count partials that pass wrote for the update buffer
+   * starting at the device address sq_base.  Every unit must then begin
+   * sq_base + a whole number of MUON_SQ_BLOCK elements and span whole blocks
+   * (its elements a multiple of MUON_SQ_BLOCK), inside the sq_count blocks;
+   * its norm is the sum of its blocks' partials (fixed order) and the inputs
+   * are not read for it.  The partials must describe the current contents of
+   * the units (the caller's ordering).  Violations: MUON_EINVAL. */
+  const double* sq_partials;
+  const void* sq_base;
+  int64_t sq_count;
 } muon_ns_params_t;
 
 /* Geometry of one weight matrix (RFC section 4A: keep the 2D shape and head
@@ -239,6 +253,22 @@ muon_status_t muon_momentum_update(muon_ctx_t* ctx, void* stream, const void* gr
                                    int32_t grad_dtype, float* momentum, void* update_out,
                                    int32_t update_dtype, int64_t numel, float beta,
                                    int32_t nesterov);
+
+/* muon_momentum_update, which also leaves the sums of squares that the
+ * Newton-Schulz normalisation needs (the survey's plan for the momentum step:
+ * per-matrix sums of squares of U come out of the same pass, so the
+ * Frobenius norms need no second read of U).  sq_partials (device,
+ * ceil(numel / MUON_SQ_BLOCK) doubles, caller-owned) receives for block b the
+ * sum of squares of update elements [b*4096, min((b+1)*4096, numel)) as
+ * stored (bf16 values when update_dtype is BF16), in binary64: every square
+ * is exact, the sum runs in a fixed order, so the partials are reproducible
+ * bit for bit.  Pass them to muon_newton_schulz_batched through
+ * muon_ns_params_t.sq_partials.  Errors: those of muon_momentum_update, and
+ * MUON_EINVAL for a NULL or overlapping sq_partials. */
+muon_status_t muon_momentum_update_sq(muon_ctx_t* ctx, void* stream, const void* grad,
+                                      int32_t grad_dtype, float* momentum, void* update_out,
+                                      int32_t update_dtype, int64_t numel, float beta,
+                                      int32_t nesterov, double* sq_partials);
 
 /* Batched Newton-Schulz over one same-shape group (blog section "Chunked
  * communication": every Muon unit stays a whole matrix; XTuner-style same-

@@ -15,7 +15,7 @@ KERNEL_CLASSES = ["momentum", "norm", "gram", "symsq", "update", "apply", "prod"
 # every symbol include/muon.h declares
 EXPORTS = [
     "muon_create", "muon_destroy", "muon_ctx_workspace_bytes", "muon_ns_params_default",
-    "muon_ns_minimax_coeffs",
+    "muon_ns_minimax_coeffs", "muon_momentum_update_sq",
     "muon_ns_workspace_bytes", "muon_plan_create", "muon_plan_num_buckets", "muon_plan_bucket",
     "muon_plan_max_workspace", "muon_plan_destroy", "muon_momentum_update",
     "muon_newton_schulz_batched", "muon_apply", "muon_status_string", "muon_last_error",
@@ -27,7 +27,9 @@ class NsParams(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int32), ("a", ctypes.c_float), ("b", ctypes.c_float),
                 ("c", ctypes.c_float), ("eps", ctypes.c_float), ("compute", ctypes.c_int32),
                 ("method", ctypes.c_int32), ("fuse", ctypes.c_int32),
-                ("coeffs", ctypes.POINTER(ctypes.c_float))]
+                ("coeffs", ctypes.POINTER(ctypes.c_float)),
+                ("sq_partials", ctypes.c_void_p), ("sq_base", ctypes.c_void_p),
+                ("sq_count", ctypes.c_int64)]
 
 
 class Shape(ctypes.Structure):
@@ -70,6 +72,7 @@ def load() -> ctypes.CDLL:
         "muon_plan_max_workspace": (sz, [vp]),
         "muon_plan_destroy": (None, [vp]),
         "muon_momentum_update": (i32, [vp, vp, vp, i32, vp, vp, i32, i64, f32, i32]),
+        "muon_momentum_update_sq": (i32, [vp, vp, vp, i32, vp, vp, i32, i64, f32, i32, vp]),
         "muon_newton_schulz_batched": (i32, [vp, vp, P(vp), i64, Shape, i32, P(NsParams), P(vp), vp]),
         "muon_apply": (i32, [vp, vp, vp, vp, i32, vp, i64, f32, f32, f32]),
         "muon_status_string": (ctypes.c_char_p, [i32]),

@@ -47,6 +47,7 @@ def _check(t: torch.Tensor, name: str, device: torch.device):
 
 
 NS_FUSE = {"auto": 0, "off": 1, "on": 2}
+SQ_BLOCK = 4096  # MUON_SQ_BLOCK
 NS_METHODS = {"quintic": 0, "gram": 1}
 
 
@@ -83,6 +84,11 @@ def ns_params(steps: int = 5, a: float = 3.4445, b: float = -4.7750, c: float = 
         p.coeffs = ctypes.cast(table, ctypes.POINTER(ctypes.c_float))
         p._table = table  # owned by the structure for as long as it lives
     return p
+
+
+def sq_blocks(numel: int) -> int:
+    """Sum-of-squares partials a momentum pass over `numel` elements writes."""
+    return (int(numel) + SQ_BLOCK - 1) // SQ_BLOCK
 
 
 def ns_workspace_bytes(rows: int, cols: int, count: int, head_rows: int = 0,
@@ -123,7 +129,10 @@ class Context:
 
     # -- the three steps ----------------------------------------------------
     def momentum_update(self, grad: torch.Tensor, momentum: torch.Tensor, update_out: torch.Tensor,
-                        beta: float = 0.95, nesterov: bool = True, stream=None):
+                        beta: float = 0.95, nesterov: bool = True, stream=None,
+                        sq_partials: Optional[torch.Tensor] = None):
+        """Momentum step; with `sq_partials` (float64, ceil(numel / 4096)
+        elements) also the per-block sums of squares of the stored update."""
         for t, n in ((grad, "grad"), (momentum, "momentum"), (update_out, "update_out")):
             _check(t, n, self.device)
         if momentum.dtype != torch.float32:
@@ -131,19 +140,37 @@ class Context:
         numel = grad.numel()
         if momentum.numel() != numel or update_out.numel() != numel:
             raise ValueError("grad, momentum and update_out must have the same numel")
-        st = self.lib.muon_momentum_update(
-            self.handle, _stream(self.device, stream), ctypes.c_void_p(grad.data_ptr()), _dtype(grad),
-            ctypes.c_void_p(momentum.data_ptr()), ctypes.c_void_p(update_out.data_ptr()),
-            _dtype(update_out), numel, float(beta), 1 if nesterov else 0)
+        args = (self.handle, _stream(self.device, stream), ctypes.c_void_p(grad.data_ptr()), _dtype(grad),
+                ctypes.c_void_p(momentum.data_ptr()), ctypes.c_void_p(update_out.data_ptr()),
+                _dtype(update_out), numel, float(beta), 1 if nesterov else 0)
+        if sq_partials is None:
+            st = self.lib.muon_momentum_update(*args)
+        else:
+            _check(sq_partials, "sq_partials", self.device)
+            if sq_partials.dtype != torch.float64 or sq_partials.numel() < sq_blocks(numel):
+                raise ValueError(f"sq_partials must be float64 with at least {sq_blocks(numel)} elements")
+            st = self.lib.muon_momentum_update_sq(*args, ctypes.c_void_p(sq_partials.data_ptr()))
         self._raise(st, "muon_momentum_update")
 
     def newton_schulz(self, mats: Sequence[torch.Tensor], out: Optional[Sequence[torch.Tensor]] = None,
                       head_rows: int = 0, params: Optional[NsParams] = None,
                       nonfinite_flag: Optional[torch.Tensor] = None, stream=None,
-                      _ptrs: Optional[Tuple] = None):
-        """Orthogonalise a same-shape group of matrices (in place when out is None)."""
+                      _ptrs: Optional[Tuple] = None, sq: Optional[Tuple] = None):
+        """Orthogonalise a same-shape group of matrices (in place when out is None).
+
+        sq = (partials, base): norms from a momentum pass's sum-of-squares
+        partials (float64 tensor) written for the update buffer `base` (a
+        tensor, or its device address) that the matrices are views of."""
         if params is None:
             params = ns_params(compute="bf16" if mats[0].dtype == torch.bfloat16 else "f32")
+        if sq is not None:
+            partials, base = sq
+            p = NsParams()
+            ctypes.memmove(ctypes.byref(p), ctypes.byref(params), ctypes.sizeof(NsParams))
+            p.sq_partials = partials.data_ptr()
+            p.sq_base = base if isinstance(base, int) else base.data_ptr()
+            p.sq_count = partials.numel()
+            params = p
         if _ptrs is None:
             _ptrs = self.pointer_arrays(mats, out)
         rows, cols = mats[0].shape[-2], mats[0].shape[-1]

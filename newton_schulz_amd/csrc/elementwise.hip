@@ -10,6 +10,13 @@
 // Every arithmetic operation is a separate IEEE binary32 operation rounded to
 // nearest-even (contraction is disabled for this file), so the results are
 // bit-identical to a binary32 evaluation of the same sequence.
+//
+// The momentum pass can also leave, per block of 4096 elements, the sum of
+// squares of the update as stored, in binary64: the Frobenius norms that
+// start the Newton-Schulz iteration then need no second read of the update.
+// Each square of a bf16 or fp32 value is exact in binary64; the sums run in a
+// fixed order (per thread, then a butterfly across each wave, then the four
+// wave sums pairwise), so the partials are reproducible bit for bit.
 #include "muon_device.h"
 #include "muon_internal.h"
 
@@ -84,15 +91,34 @@ __device__ __forceinline__ void momentum_one(float g, float& m, float& u, float 
 
 // one-shot vector path: EW_U groups of 8 elements per thread, EW_BS threads
 constexpr int EW_BS = 256, EW_U = 2;  // 4096 elements per workgroup
+static_assert(EW_BS * EW_U * 8 == MUON_SQ_BLOCK, "a workgroup's range is one partial block");
 
-template <typename G, typename U>
+// exact square of a stored value
+__device__ __forceinline__ double sq64(float v) {
+  const double d = static_cast<double>(v);
+  return d * d;
+}
+
+// Sum of the 256 threads' values in a fixed order; thread 0 gets the total.
+__device__ __forceinline__ double block_sum(double v) {
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) v += __shfl_xor(v, k, 64);
+  __shared__ double ws[EW_BS / 64];
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (ws[0] + ws[1]) + (ws[2] + ws[3]);
+}
+
+template <typename G, typename U, bool SQ>
 __global__ __launch_bounds__(EW_BS) void momentum_vec_kernel(const G* __restrict__ grad,
                                                              float* __restrict__ mom,
                                                              U* __restrict__ upd, int64_t numel,
-                                                             float beta, float c1, int nesterov) {
+                                                             float beta, float c1, int nesterov,
+                                                             double* __restrict__ sq) {
   const bool nes = nesterov != 0;
   const int64_t nvec = numel / 8;
   const int64_t base = static_cast<int64_t>(blockIdx.x) * (EW_U * EW_BS) + threadIdx.x;
+  double acc = 0.0;
   Vec8<G> g[EW_U];
   Vec8<float> m[EW_U];
 #pragma unroll
@@ -113,16 +139,45 @@ __global__ __launch_bounds__(EW_BS) void momentum_vec_kernel(const G* __restrict
       // the momentum is next read a whole step later: do not keep it cached
       m[k].template store<true>(mom + 8 * i);
       u.store(upd + 8 * i);
+      if (SQ) {
+        double q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = sq64(muon::Elem<U>::round(u.v[e]));
+        acc += ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+      }
     }
   }
-  if (blockIdx.x == gridDim.x - 1) {  // the last numel % 8 elements
+  // The last numel % 8 elements; they lie in the last workgroup's range (the
+  // grid has one workgroup per started 4096 elements).
+  if (blockIdx.x == gridDim.x - 1) {
     for (int64_t i = nvec * 8 + threadIdx.x; i < numel; i += EW_BS) {
       float mm = mom[i], u;
       momentum_one(muon::Elem<G>::load(grad + i), mm, u, beta, c1, nes);
       mom[i] = mm;
       muon::Elem<U>::store(upd + i, u);
+      if (SQ) acc += sq64(muon::Elem<U>::round(u));
     }
   }
+  if (SQ) {
+    const double t = block_sum(acc);
+    if (threadIdx.x == 0) sq[blockIdx.x] = t;
+  }
+}
+
+// Partials of an update written by the scalar path: workgroup b sums the
+// squares of elements [4096 b, 4096 b + 4096), thread t elements t + 256 j
+// in j order.
+template <typename U>
+__global__ __launch_bounds__(EW_BS) void sq_blocks_kernel(const U* __restrict__ upd, int64_t numel,
+                                                          double* __restrict__ sq) {
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * MUON_SQ_BLOCK;
+  double acc = 0.0;
+  for (int j = 0; j < MUON_SQ_BLOCK / EW_BS; ++j) {
+    const int64_t i = b0 + j * EW_BS + threadIdx.x;
+    if (i < numel) acc += sq64(muon::Elem<U>::load(upd + i));
+  }
+  const double t = block_sum(acc);
+  if (threadIdx.x == 0) sq[blockIdx.x] = t;
 }
 
 template <typename G, typename U>
@@ -205,9 +260,10 @@ __global__ __launch_bounds__(256) void apply_scalar_kernel(float* __restrict__ m
   }
 }
 
-// one workgroup per 4096 elements (at least one, for the scalar tail)
+// one workgroup per started 4096 elements; the last one also takes the
+// scalar tail, which lies in its range
 inline unsigned vec_grid(int64_t numel) {
-  const int64_t blocks = (numel / 8 + EW_U * EW_BS - 1) / (EW_U * EW_BS);
+  const int64_t blocks = (numel + MUON_SQ_BLOCK - 1) / MUON_SQ_BLOCK;
   return static_cast<unsigned>(blocks < 1 ? 1 : blocks);
 }
 
@@ -226,18 +282,27 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 
 hipError_t launch_momentum(hipStream_t s, int cus, const void* grad, int gdt, float* mom,
                            void* upd, int udt, int64_t numel, float beta, float c1,
-                           int nesterov) {
+                           int nesterov, double* sq) {
   if (numel <= 0) return hipSuccess;
-  if (numel / 8 >= (int64_t{1} << 40)) return hipErrorInvalidValue;  // beyond a 1-D grid
+  // one workgroup per 4096 elements must fit a 1-D grid
+  if ((numel + MUON_SQ_BLOCK - 1) / MUON_SQ_BLOCK > 0x7fffffff) return hipErrorInvalidValue;
   const bool vec = aligned(grad, 16) && aligned(mom, 16) && aligned(upd, 16);
-#define MUON_MOM(G, U)                                                                       \
-  do {                                                                                       \
-    if (vec)                                                                                 \
-      momentum_vec_kernel<G, U><<<vec_grid(numel), EW_BS, 0, s>>>(                           \
-          static_cast<const G*>(grad), mom, static_cast<U*>(upd), numel, beta, c1, nesterov); \
-    else                                                                                     \
-      momentum_scalar_kernel<G, U><<<stream_grid(numel, cus), 256, 0, s>>>(                  \
-          static_cast<const G*>(grad), mom, static_cast<U*>(upd), numel, beta, c1, nesterov); \
+#define MUON_MOM(G, U)                                                                        \
+  do {                                                                                        \
+    if (vec && sq)                                                                            \
+      momentum_vec_kernel<G, U, true><<<vec_grid(numel), EW_BS, 0, s>>>(                      \
+          static_cast<const G*>(grad), mom, static_cast<U*>(upd), numel, beta, c1, nesterov,  \
+          sq);                                                                                \
+    else if (vec)                                                                             \
+      momentum_vec_kernel<G, U, false><<<vec_grid(numel), EW_BS, 0, s>>>(                     \
+          static_cast<const G*>(grad), mom, static_cast<U*>(upd), numel, beta, c1, nesterov,  \
+          nullptr);                                                                           \
+    else                                                                                      \
+      momentum_scalar_kernel<G, U><<<stream_grid(numel, cus), 256, 0, s>>>(                   \
+          static_cast<const G*>(grad), mom, static_cast<U*>(upd), numel, beta, c1, nesterov);  \
+    if (!vec && sq)                                                                           \
+      sq_blocks_kernel<U><<<vec_grid(numel), EW_BS, 0, s>>>(static_cast<const U*>(upd), numel, \
+                                                             sq);                             \
   } while (0)
   if (gdt == 1 && udt == 1) MUON_MOM(bf16_t, bf16_t);
   else if (gdt == 1 && udt == 0) MUON_MOM(bf16_t, float);
@@ -250,7 +315,7 @@ hipError_t launch_momentum(hipStream_t s, int cus, const void* grad, int gdt, fl
 hipError_t launch_apply(hipStream_t s, int cus, float* master, const void* upd, int udt,
                         void* wbf, int64_t numel, float eta, float decay, int has_wd) {
   if (numel <= 0) return hipSuccess;
-  if (numel / 8 >= (int64_t{1} << 40)) return hipErrorInvalidValue;  // beyond a 1-D grid
+  if ((numel + MUON_SQ_BLOCK - 1) / MUON_SQ_BLOCK > 0x7fffffff) return hipErrorInvalidValue;
   const bool vec = aligned(master, 16) && aligned(upd, 16) && (wbf == nullptr || aligned(wbf, 16));
   bf16_t* wb = static_cast<bf16_t*>(wbf);
 #define MUON_APPLY(U, B)                                                                         \

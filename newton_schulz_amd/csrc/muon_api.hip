@@ -141,6 +141,9 @@ void muon_ns_params_default(muon_ns_params_t* p) {
   p->method = MUON_NS_QUINTIC;
   p->fuse = MUON_FUSE_AUTO;
   p->coeffs = nullptr;
+  p->sq_partials = nullptr;
+  p->sq_base = nullptr;
+  p->sq_count = 0;
 }
 
 size_t muon_ctx_workspace_bytes(const muon_ctx_t* ctx) { return ctx ? ctx->ws_bytes : 0; }
@@ -238,10 +241,9 @@ muon_status_t muon_timing_read(muon_ctx_t* c, int32_t cls, double* total_ms, int
   return MUON_OK;
 }
 
-muon_status_t muon_momentum_update(muon_ctx_t* c, void* stream, const void* grad,
-                                   int32_t grad_dtype, float* momentum, void* update_out,
-                                   int32_t update_dtype, int64_t numel, float beta,
-                                   int32_t nesterov) {
+static muon_status_t momentum_impl(muon_ctx_t* c, void* stream, const void* grad, int32_t grad_dtype,
+                            float* momentum, void* update_out, int32_t update_dtype,
+                            int64_t numel, float beta, int32_t nesterov, double* sq) {
   if (c == nullptr) return MUON_EINVAL;
   if (numel < 0) return fail(c, MUON_EINVAL, "numel < 0");
   if (!is_dtype(grad_dtype) || !is_dtype(update_dtype)) return fail(c, MUON_EDTYPE, "dtype");
@@ -257,15 +259,40 @@ muon_status_t muon_momentum_update(muon_ctx_t* c, void* stream, const void* grad
       (reinterpret_cast<uintptr_t>(momentum) % 4) ||
       (reinterpret_cast<uintptr_t>(update_out) % esize(update_dtype)))
     return fail(c, MUON_EINVAL, "misaligned pointer");
+  if (sq != nullptr) {
+    const size_t qb = static_cast<size_t>((numel + MUON_SQ_BLOCK - 1) / MUON_SQ_BLOCK) * 8;
+    if (reinterpret_cast<uintptr_t>(sq) % 8) return fail(c, MUON_EINVAL, "misaligned sq_partials");
+    if (ranges_overlap(sq, qb, grad, nb * esize(grad_dtype)) || ranges_overlap(sq, qb, momentum, nb * 4) ||
+        ranges_overlap(sq, qb, update_out, nb * esize(update_dtype)))
+      return fail(c, MUON_EINVAL, "sq_partials overlaps a buffer");
+  }
   DeviceGuard g(c->device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float c1 = 1.0f - beta;
   const long tk = tstart(c, s, MUON_K_MOMENTUM);
   const hipError_t e = launch_momentum(s, c->cus, grad, grad_dtype, momentum, update_out,
-                                       update_dtype, numel, beta, c1, nesterov ? 1 : 0);
+                                       update_dtype, numel, beta, c1, nesterov ? 1 : 0, sq);
   tstop(c, s, tk);
   if (e != hipSuccess) return hip_fail(c, e, "momentum launch");
   return MUON_OK;
+}
+
+muon_status_t muon_momentum_update(muon_ctx_t* c, void* stream, const void* grad,
+                                   int32_t grad_dtype, float* momentum, void* update_out,
+                                   int32_t update_dtype, int64_t numel, float beta,
+                                   int32_t nesterov) {
+  return momentum_impl(c, stream, grad, grad_dtype, momentum, update_out, update_dtype, numel,
+                       beta, nesterov, nullptr);
+}
+
+muon_status_t muon_momentum_update_sq(muon_ctx_t* c, void* stream, const void* grad,
+                                      int32_t grad_dtype, float* momentum, void* update_out,
+                                      int32_t update_dtype, int64_t numel, float beta,
+                                      int32_t nesterov, double* sq_partials) {
+  if (c == nullptr) return MUON_EINVAL;
+  if (sq_partials == nullptr) return fail(c, MUON_EINVAL, "sq_partials NULL");
+  return momentum_impl(c, stream, grad, grad_dtype, momentum, update_out, update_dtype, numel,
+                       beta, nesterov, sq_partials);
 }
 
 muon_status_t muon_apply(muon_ctx_t* c, void* stream, float* master, const void* update,
@@ -366,10 +393,25 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     if ((reinterpret_cast<uintptr_t>(mats[i]) % es) || (out && reinterpret_cast<uintptr_t>(out[i]) % es))
       return fail(c, MUON_EINVAL, "misaligned matrix");
   }
-  if (L.total > c->ws_bytes) return fail(c, MUON_EWORKSPACE, "workspace too small for this call");
   const int64_t per = L.units / count;
   const int64_t unit_elems = L.ur * L.uc;
   const int64_t unit_bytes = unit_elems * static_cast<int64_t>(es);
+  // norms from the momentum pass: every unit on whole blocks inside the partials
+  const int64_t block_bytes = int64_t{MUON_SQ_BLOCK} * static_cast<int64_t>(es);
+  if (prm->sq_partials != nullptr) {
+    if (prm->sq_base == nullptr || prm->sq_count < 0 ||
+        reinterpret_cast<uintptr_t>(prm->sq_partials) % 8 || unit_elems % MUON_SQ_BLOCK)
+      return fail(c, MUON_EINVAL, "sq_partials: units must span whole blocks");
+    const uintptr_t base = reinterpret_cast<uintptr_t>(prm->sq_base);
+    const int64_t nblk = per * (unit_elems / MUON_SQ_BLOCK);
+    for (int64_t i = 0; i < count; ++i) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(mats[i]);
+      if (a < base || (a - base) % static_cast<uintptr_t>(block_bytes) ||
+          static_cast<int64_t>((a - base) / static_cast<uintptr_t>(block_bytes)) > prm->sq_count - nblk)
+        return fail(c, MUON_EINVAL, "sq_partials do not cover a matrix on block boundaries");
+    }
+  }
+  if (L.total > c->ws_bytes) return fail(c, MUON_EWORKSPACE, "workspace too small for this call");
   const void* const* outp = out ? reinterpret_cast<const void* const*>(out) : mats;
 
   UnitsRef in = describe(mats, count, per, unit_bytes);
@@ -457,6 +499,10 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   na.zflag = zflag;
   na.nonfinite = nonfinite_flag;
   na.eps = prm->eps;
+  na.sq = prm->sq_partials;
+  na.sq_base = static_cast<const char*>(prm->sq_base);
+  na.block_bytes = block_bytes;
+  na.blocks_per_unit = unit_elems / MUON_SQ_BLOCK;
   long tk = tstart(c, s, MUON_K_NORM);
   e = launch_norm(s, na, io_bf16, al && (unit_elems % 8 == 0));
   tstop(c, s, tk);

@@ -44,6 +44,12 @@ struct NsNormArgs {
   int* zflag;          // [units] : ||Y||_F == 0
   int* nonfinite;      // device flag or nullptr
   float eps;
+  // norms from momentum partials instead of a pass over `in`: unit u's blocks
+  // start at (address of unit u - sq_base) / block_bytes
+  const double* sq;    // or nullptr
+  const char* sq_base;
+  int64_t block_bytes;
+  int64_t blocks_per_unit;
 };
 
 // The whole iteration (quintic, or its Gram form) of wide units with
@@ -65,7 +71,7 @@ hipError_t launch_ns_small(hipStream_t s, const NsSmallArgs& a);
 
 hipError_t launch_momentum(hipStream_t s, int cus, const void* grad, int gdt, float* mom,
                            void* upd, int udt, int64_t numel, float beta, float c1,
-                           int nesterov);
+                           int nesterov, double* sq);
 hipError_t launch_apply(hipStream_t s, int cus, float* master, const void* upd, int udt,
                         void* wbf, int64_t numel, float eta, float decay, int has_wd);
 

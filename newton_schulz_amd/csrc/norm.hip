@@ -97,6 +97,14 @@ __global__ __launch_bounds__(256) void norm_partial_kernel(NsNormArgs a) {
   if (threadIdx.x == 0) a.partial[u * a.parts + p] = red[0];
 }
 
+// Unit u's scale, zero flag and non-finite report from its sum of squares.
+__device__ __forceinline__ void finish_unit(const NsNormArgs& a, int64_t u, double s) {
+  const double nrm = sqrt(s);
+  a.scale[u] = static_cast<float>(1.0 / (nrm + static_cast<double>(a.eps)));
+  a.zflag[u] = (s == 0.0) ? 1 : 0;
+  if (a.nonfinite && !isfinite(s)) atomicOr(a.nonfinite, 1);
+}
+
 // One wave per unit: lane l adds parts l, l + 64, l + 128, ... in order, then
 // an xor butterfly adds the 64 lane sums (both partners of a step form the
 // same sum, so every lane ends with the same, fixed-order total).
@@ -108,11 +116,38 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(NsNormArgs a) {
   for (int p = lane; p < a.parts; p += 64) s += a.partial[u * a.parts + p];
 #pragma unroll
   for (int k = 32; k > 0; k >>= 1) s += __shfl_xor(s, k, 64);
-  if (lane != 0) return;
-  const double nrm = sqrt(s);
-  a.scale[u] = static_cast<float>(1.0 / (nrm + static_cast<double>(a.eps)));
-  a.zflag[u] = (s == 0.0) ? 1 : 0;
-  if (a.nonfinite && !isfinite(s)) atomicOr(a.nonfinite, 1);
+  if (lane == 0) finish_unit(a, u, s);
+}
+
+// The same from the momentum pass's per-block partials, one workgroup per
+// unit: unit u owns blocks b0 .. b0 + blocks_per_unit - 1, b0 = (address of
+// u - sq_base) / block_bytes (the host has checked that every unit starts on
+// a block boundary inside the partials).  Thread t adds blocks t, t + 256,
+// ... in order, eight loads in flight ahead of the adds; then a butterfly per
+// wave and the four wave sums pairwise.
+__global__ __launch_bounds__(256) void norm_from_blocks_kernel(NsNormArgs a) {
+  const int64_t u = blockIdx.x;
+  const int64_t b0 = (reinterpret_cast<const char*>(mat_at(a.in, u)) - a.sq_base) / a.block_bytes;
+  const double* q = a.sq + b0;
+  const int64_t nb = a.blocks_per_unit;
+  constexpr int R = 8;
+  double s = 0.0;
+  for (int64_t p0 = threadIdx.x; p0 < nb; p0 += R * 256) {
+    double v[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t p = p0 + r * 256;
+      v[r] = p < nb ? q[p] : 0.0;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) s += v[r];
+  }
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) s += __shfl_xor(s, k, 64);
+  __shared__ double ws[4];
+  if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) finish_unit(a, u, (ws[0] + ws[1]) + (ws[2] + ws[3]));
 }
 
 template <typename T>
@@ -139,6 +174,11 @@ static MatRef shifted(MatRef r, int64_t u0) {
 
 hipError_t launch_norm(hipStream_t s, const NsNormArgs& a, int io_bf16, bool vec) {
   if (a.units == 0) return hipSuccess;
+  if (a.sq != nullptr) {
+    if (a.units > 0x7fffffff) return hipErrorInvalidValue;
+    norm_from_blocks_kernel<<<static_cast<unsigned>(a.units), 256, 0, s>>>(a);
+    return hipGetLastError();
+  }
   constexpr int64_t kMaxY = 65535;
   for (int64_t u0 = 0; u0 < a.units; u0 += kMaxY) {
     NsNormArgs c = a;

@@ -6,10 +6,14 @@ sections "Memory control" item 2 and "DBuffer").  Per micro-bucket the step
 enqueues, on one stream and with no host synchronisation:
     momentum (+ Nesterov) -> batched Newton-Schulz per shape group -> apply
 (the blog's recommended chunked-execution pseudocode, minus the all-to-all
-exchanges, which one device does not need).  The Newton-Schulz input/output
-buffer holds one micro-bucket, so device memory beyond the caller's state is
-cap-bounded: update buffer <= cap (full-byte caps) plus the context
-workspace <= max over micro-buckets of the Newton-Schulz workspace.
+exchanges, which one device does not need).  The momentum pass also leaves
+the sums of squares of every 4096-element block of the update, from which the
+Newton-Schulz call takes each matrix's Frobenius norm without reading the
+update again (groups whose matrices do not lie on whole blocks read it).  The
+Newton-Schulz input/output buffer holds one micro-bucket, so device memory
+beyond the caller's state is cap-bounded: update buffer <= cap (full-byte
+caps), its partials (8 bytes per 4096 elements), plus the context workspace
+<= max over micro-buckets of the Newton-Schulz workspace.
 """
 from __future__ import annotations
 
@@ -17,7 +21,7 @@ from typing import List, Optional, Sequence, Tuple
 
 import torch
 
-from .api import Context, Plan, ns_params
+from .api import SQ_BLOCK, Context, Plan, ns_params, sq_blocks
 
 
 class MuonStep:
@@ -26,7 +30,7 @@ class MuonStep:
                  grad_dtype: torch.dtype = torch.bfloat16, cap_bytes: int = 512 << 20,
                  cap_kind: str = "full", ns_steps: int = 5, keep_bf16_weights: bool = False,
                  weight_decay: float = 0.0, scale: float = 1.0, ns_method: str = "quintic",
-                 ns_coeffs=None):
+                 ns_coeffs=None, norms_from_momentum: bool = True):
         self.device = torch.device(device if device is not None else "cuda")
         if self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -55,6 +59,8 @@ class MuonStep:
         self.weight_bf16 = torch.zeros(off, dtype=torch.bfloat16, device=dev) if keep_bf16_weights else None
         max_bucket = max((b.numel for b in self.plan.buckets), default=0)
         self.update = torch.empty(max(max_bucket, 1), dtype=self.cdtype, device=dev)
+        # per-4096-element sums of squares of the update, from the momentum pass
+        self.sq = torch.empty(max(sq_blocks(max_bucket), 1), dtype=torch.float64, device=dev)
         self.ctx = Context(dev, self.plan.max_workspace)
 
         # per micro-bucket: element range and shape groups with cached pointer arrays
@@ -71,9 +77,14 @@ class MuonStep:
                     k += 1
                 r, c, h = self.shapes[b.indices[j]]
                 mats = [self._uview(self.offset[i] - lo, r, c) for i in b.indices[j:k]]
-                groups.append((h, mats, self.ctx.pointer_arrays(mats)))
+                # norms from the momentum partials when every unit of the group
+                # starts on, and spans, whole 4096-element blocks
+                unit = (h if h else r) * c
+                whole = norms_from_momentum and unit % SQ_BLOCK == 0 and all(
+                    (self.offset[i] - lo) % SQ_BLOCK == 0 for i in b.indices[j:k])
+                groups.append((h, mats, self.ctx.pointer_arrays(mats), whole))
                 j = k
-            self._work.append((lo, hi, groups))
+            self._work.append((lo, hi, groups, any(g[3] for g in groups)))
             pos = hi
         assert pos == self.numel
 
@@ -88,16 +99,17 @@ class MuonStep:
     def momentum_only(self, stream=None):
         """Momentum update of every matrix, without Newton-Schulz or apply
         (used to pre-fill momentum); the update output is discarded."""
-        for lo, hi, _ in self._work:
+        for lo, hi, _, _ in self._work:
             self.ctx.momentum_update(self.grad[lo:hi], self.momentum[lo:hi], self.update[:hi - lo],
                                      self.beta, self.nesterov, stream)
 
     def step(self, stream=None, nonfinite_flag: Optional[torch.Tensor] = None):
-        for lo, hi, groups in self._work:
+        for lo, hi, groups, want_sq in self._work:
             upd = self.update[:hi - lo]
             self.ctx.momentum_update(self.grad[lo:hi], self.momentum[lo:hi], upd, self.beta,
-                                     self.nesterov, stream)
-            for h, mats, ptrs in groups:
-                self.ctx.newton_schulz(mats, None, h, self.params, nonfinite_flag, stream, _ptrs=ptrs)
+                                     self.nesterov, stream, sq_partials=self.sq if want_sq else None)
+            for h, mats, ptrs, whole in groups:
+                self.ctx.newton_schulz(mats, None, h, self.params, nonfinite_flag, stream, _ptrs=ptrs,
+                                       sq=(self.sq, upd) if whole else None)
             wb = self.weight_bf16[lo:hi] if self.weight_bf16 is not None else None
             self.ctx.apply(self.master[lo:hi], upd, self.lr, self.scale, self.weight_decay, wb, stream)

@@ -62,7 +62,8 @@ def test_struct_and_enum_mirrors_match_header():
     count = int(re.search(r"MUON_K_COUNT\s*=\s*(\d+)", text).group(1))
     assert len(_lib.KERNEL_CLASSES) == count
     assert int(re.search(r"MUON_NS_GRAM\s*=\s*(\d+)", text).group(1)) == 1
-    from newton_schulz_amd.api import NS_FUSE
+    from newton_schulz_amd.api import NS_FUSE, SQ_BLOCK
+    assert int(re.search(r"#define MUON_SQ_BLOCK\s+(\d+)", text).group(1)) == SQ_BLOCK
     for name, v in NS_FUSE.items():
         assert int(re.search(rf"MUON_FUSE_{name.upper()}\s*=\s*(\d+)", text).group(1)) == v
 
@@ -73,8 +74,11 @@ def test_null_context_rejected():
     lib.muon_ns_params_default(ctypes.byref(p))
     assert (p.steps, round(p.a, 4), round(p.b, 4), round(p.c, 4), p.compute) == (5, 3.4445, -4.775, 2.0315, 1)
     assert p.method == 0 and p.fuse == 0 and not p.coeffs
+    assert not p.sq_partials and not p.sq_base and p.sq_count == 0
     assert lib.muon_momentum_update(None, None, None, 1, None, None, 1, 10, 0.95, 1) == _lib.MUON_EINVAL
     assert lib.muon_apply(None, None, None, None, 1, None, 10, 0.02, 1.0, 0.0) == _lib.MUON_EINVAL
+    assert lib.muon_momentum_update_sq(None, None, None, 1, None, None, 1, 10, 0.95, 1,
+                                       None) == _lib.MUON_EINVAL
     assert lib.muon_newton_schulz_batched(None, None, None, 1, _lib.Shape(8, 8, 0), 1, ctypes.byref(p),
                                           None, None) == _lib.MUON_EINVAL
 
