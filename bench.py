@@ -171,6 +171,8 @@ def main():
                     help="fixed quintic (a, b, c), or the per-iteration minimax schedule")
     ap.add_argument("--ns-steps", type=int, default=0,
                     help="Newton-Schulz iterations (default: the workload's)")
+    ap.add_argument("--ns-fuse", default="auto", choices=["auto", "off", "on"],
+                    help="whole-iteration fusion of small units (muon_fuse_t)")
     ap.add_argument("--norms", default="momentum", choices=["momentum", "pass"],
                     help="Frobenius norms from the momentum pass's partials, or a separate read")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -205,7 +207,7 @@ def main():
                   grad_dtype=w.grad_dtype, cap_bytes=w.cap_bytes, cap_kind=w.cap_kind,
                   ns_steps=w.ns_steps, keep_bf16_weights=keep_bf16, ns_method=args.ns_method,
                   ns_coeffs=None if args.ns_coeffs == "fixed" else args.ns_coeffs,
-                  norms_from_momentum=args.norms == "momentum")
+                  norms_from_momentum=args.norms == "momentum", ns_fuse=args.ns_fuse)
     g = torch.Generator(device=dev).manual_seed(w.seed)
     for i, W0 in enumerate(synth.draw_weights(w, g, dev)):
         ms.view(ms.master, i).copy_(W0)
@@ -321,6 +323,7 @@ def main():
         "config": {"workload": w.name, "matrices": len(w.mats), "muon_params": numel,
                    "ns_units": len(units), "ns_steps": w.ns_steps, "ns_method": args.ns_method,
                    "ns_coeffs": args.ns_coeffs, "norms": args.norms,
+                   "ns_fuse": args.ns_fuse,
                    "micro_bucket_cap_bytes": w.cap_bytes, "cap_kind": w.cap_kind,
                    "micro_buckets": len(ms.plan.buckets), "workspace_bytes": ms.plan.max_workspace,
                    "parallelism": "single GPU"},

@@ -30,7 +30,7 @@ class MuonStep:
                  grad_dtype: torch.dtype = torch.bfloat16, cap_bytes: int = 512 << 20,
                  cap_kind: str = "full", ns_steps: int = 5, keep_bf16_weights: bool = False,
                  weight_decay: float = 0.0, scale: float = 1.0, ns_method: str = "quintic",
-                 ns_coeffs=None, norms_from_momentum: bool = True):
+                 ns_coeffs=None, norms_from_momentum: bool = True, ns_fuse: str = "auto"):
         self.device = torch.device(device if device is not None else "cuda")
         if self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -39,7 +39,8 @@ class MuonStep:
         self.weight_decay, self.scale = weight_decay, scale
         self.compute = compute
         self.cdtype = torch.bfloat16 if compute == "bf16" else torch.float32
-        self.params = ns_params(steps=ns_steps, compute=compute, method=ns_method, coeffs=ns_coeffs)
+        self.params = ns_params(steps=ns_steps, compute=compute, method=ns_method, coeffs=ns_coeffs,
+                                fuse=ns_fuse)
         cus = torch.cuda.get_device_properties(self.device).multi_processor_count
         self.plan = Plan(self.shapes, cap_bytes, cap_kind, compute, compute_units=cus)
 
