@@ -136,9 +136,12 @@ __global__ __launch_bounds__(EW_BS) void momentum_vec_kernel(const G* __restrict
       Vec8<U> u;
 #pragma unroll
       for (int e = 0; e < 8; ++e) momentum_one(g[k].v[e], m[k].v[e], u.v[e], beta, c1, nes);
-      // the momentum is next read a whole step later: do not keep it cached
+      // the momentum is next read a whole step later: do not keep it cached;
+      // U is read next by a launch that streams far more than the caches
+      // hold (non-temporal stores measured 1% faster here, and no slower for
+      // the Newton-Schulz launch that reads U)
       m[k].template store<true>(mom + 8 * i);
-      u.store(upd + 8 * i);
+      u.template store<true>(upd + 8 * i);
       if (SQ) {
         double q[8];
 #pragma unroll

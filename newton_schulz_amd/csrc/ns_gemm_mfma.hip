@@ -455,7 +455,6 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
     // reads; blocks of 32 columns x 16 rows, one per wave at a time
     constexpr int BJ = BN / 32, BI = BM / 16;
     const int gq = elane >> 4, jx = elane & 15;
-#pragma unroll 4
     for (int b = wave; b < BJ * BI; b += NW) {
       const int jb = (b % BJ) * 32, ib = (b / BJ) * 16;
       const int col = jb + 16 * (gq & 1) + 4 * (jx & 3);
