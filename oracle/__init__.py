@@ -5,5 +5,5 @@ from .muon_oracle import (  # noqa: F401
     momentum_ref, ns_ref, ns_ref_heads, split_heads, apply_ref,
     muon_step_ref, rel_fro,
     MINIMAX_LO, MINIMAX_MARGIN, LIMIT_QUINTIC, minimax_quintic, minimax_schedule,
-    quintic_eval,
+    quintic_eval, sumsq_blocks,
 )

@@ -44,7 +44,8 @@ Pins (tests/test_oracle_*.py, run without a GPU) tie each function to facts
 other than itself: the SVD closed form of the odd matrix polynomial, diagonal
 and rank-1 inputs, transpose / sign / scale / orthogonal symmetries, an
 independent Gram-recursion evaluation, exact rational emulation of the
-binary32 momentum and apply sequences, torch's CPU bfloat16 cast, and for the
+binary32 momentum and apply sequences, torch's CPU bfloat16 cast, exact
+rational sums of squares per block, and for the
 per-iteration coefficients a linear-programme solution of the same best
 approximation, the alternation property and the closed-form limit polynomial.
 """
@@ -115,6 +116,26 @@ def momentum_ref(g, M, beta: float = 0.95, nesterov: bool = True):
     else:
         U = M_new.copy()
     return M_new, U
+
+
+# ---------------------------------------------------------------------------
+# Sums of squares per block (the Frobenius norms' raw material).
+# ---------------------------------------------------------------------------
+def sumsq_blocks(u, block: int = 4096):
+    """Sum of squares of each run of `block` consecutive values (the last run
+    may be short), correctly rounded to binary64.
+
+    X_0 = Y / (||Y||_F + eps) needs ||Y||_F^2 = sum of squares of Y's
+    elements (RFC section 2; blog "Muon Optimizer + FSDP", Memory control
+    item 4 keeps such scalars in FP32 or wider).  Summed per block, a unit
+    that spans whole blocks gets its norm from its blocks.  Squares of
+    binary32 values are exact in binary64 and math.fsum rounds the exact sum
+    once, so the result depends on the values only, not on any order.
+    """
+    import math
+    v = np.asarray(u, dtype=np.float32).astype(np.float64).ravel()
+    return np.array([math.fsum((v[b:b + block] ** 2).tolist()) for b in range(0, len(v), block)],
+                    dtype=np.float64)
 
 
 # ---------------------------------------------------------------------------

@@ -5,13 +5,12 @@ squares of the update as stored; Newton-Schulz then takes each unit's
 Frobenius norm from its blocks instead of reading the update again.  Bars:
 momentum and update bit-exact against the oracle as for the plain entry
 point; every partial within 1e-12 (relative) of the exactly rounded sum of
-its block's squares (math.fsum over the stored values), and bit-identical
+its block's squares (oracle.sumsq_blocks over the stored values), and bit-identical
 from call to call; Newton-Schulz with partials within 1e-3 of the call that
 reads its input for the norm (the two sums differ only in rounding order,
 so the float scales almost always agree bit for bit) and within the oracle
 bar.
 """
-import math
 import sys
 
 import numpy as np
@@ -50,12 +49,6 @@ def gen(seed):
     return torch.Generator(device=DEV).manual_seed(seed)
 
 
-def exact_block_sums(u: np.ndarray):
-    """Correctly rounded sum of squares per 4096-element block (values as stored)."""
-    u = u.astype(np.float64)
-    return [math.fsum((u[b:b + SQ_BLOCK] ** 2).tolist()) for b in range(0, len(u), SQ_BLOCK)]
-
-
 @pytest.mark.parametrize("gdt,udt", [(torch.bfloat16, torch.bfloat16), (torch.float32, torch.float32),
                                      (torch.float32, torch.bfloat16)])
 # vector path: whole blocks, a partial last block, a scalar tail that opens a
@@ -79,7 +72,7 @@ def test_momentum_sq_partials(ctx, gdt, udt, numel, offset):
     stored = oracle.bf16_round(u_ref) if udt == torch.bfloat16 else u_ref
     assert np.array_equal(host(upd), stored)
     got = sq.cpu().numpy()
-    want = np.array(exact_block_sums(stored))
+    want = oracle.sumsq_blocks(stored, SQ_BLOCK)
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=0)
     # reproducible bit for bit
     mom2 = mom0.clone()

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import apply_ref, bf16_bits, bf16_from_bits, bf16_round, momentum_ref
+from oracle import apply_ref, bf16_bits, bf16_from_bits, bf16_round, momentum_ref, sumsq_blocks
 
 # ---------------------------------------------------------------------------
 # exact binary32 rounding from the definition
@@ -173,3 +173,28 @@ def test_bf16_round_matches_torch_cast():
     assert np.array_equal(bf16_round(bf16_from_bits(ours)), bf16_from_bits(ours))
     # NaN stays NaN
     assert np.isnan(bf16_round(np.array([np.nan], dtype=np.float32)))[0]
+
+
+# ---------------------------------------------------------------------------
+# sums of squares per block
+# ---------------------------------------------------------------------------
+def test_sumsq_blocks_exact_rational():
+    """Against exact rational arithmetic: the binary64 value nearest to the
+    true sum of squares of each block."""
+    rng = np.random.default_rng(11)
+    u = (rng.standard_normal(3 * 64 + 17) * 10.0 ** rng.uniform(-8, 3, 3 * 64 + 17)).astype(np.float32)
+    got = sumsq_blocks(u, 64)
+    assert len(got) == 4
+    for b in range(4):
+        exact = sum((Fraction(float(x)) ** 2 for x in u[64 * b:64 * b + 64]), Fraction(0))
+        assert got[b] == float(exact)        # float(Fraction) rounds to nearest
+
+
+def test_sumsq_blocks_closed_forms():
+    assert sumsq_blocks(np.ones(10000, np.float32)).tolist() == [4096.0, 4096.0, 1808.0]
+    assert sumsq_blocks(np.zeros(5, np.float32)).tolist() == [0.0]
+    x = np.arange(1, 4097, dtype=np.float32)
+    n = 4096
+    assert sumsq_blocks(x)[0] == n * (n + 1) * (2 * n + 1) / 6
+    assert np.isinf(sumsq_blocks(np.array([1.0, np.inf], np.float32))[0])
+    assert np.isnan(sumsq_blocks(np.array([1.0, np.nan], np.float32))[0])
