@@ -4,7 +4,8 @@
  * The step, per whole 2D weight matrix (blog "Muon Optimizer + FSDP",
  * section "Background: the conflict between FSDP and Muon"):
  *
- *     M_t = momentum_update(grad)      -> muon_momentum_update
+ *     M_t = momentum_update(grad)      -> muon_momentum_update (_sq: also the
+ *                                         sums of squares for the norms)
  *     U_t = NewtonSchulz(M_t)          -> muon_newton_schulz_batched
  *     W_t = W_t - lr * U_t             -> muon_apply
  *
