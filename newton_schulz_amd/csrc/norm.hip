@@ -2,12 +2,16 @@
 //
 // X_0 = Y / (||Y||_F + eps) starts the iteration; the blog "Muon Optimizer +
 // FSDP" (section "Memory control", item 4) advises keeping the normalisation
-// scalars in FP32 even when the buffers are BF16.  Here the squares are formed
-// exactly (bf16^2 fits fp32; fp32^2 fits fp64) and summed in fp64 in a fixed
-// order: per thread over its interleaved pieces, then a fixed shared-memory
-// tree, then the parts of a unit in index order.  No atomics take part in the sum, so the scale is
-// bit-reproducible.  The scale 1/(||Y|| + eps) is folded into the first
-// iteration's epilogues instead of rewriting Y.
+// scalars in FP32 even when the buffers are BF16.  The squares are exact
+// (bf16^2 fits fp32; fp32^2 fits fp64) and summed in fp64 in a fixed order,
+// with no atomics, so the scale is bit-reproducible.  Two sources:
+//   - the momentum pass's per-4096-element partials (norm_from_blocks_kernel
+//     adds a unit's blocks), when the caller hands them over: no second read;
+//   - otherwise a pass over the units: per thread over its interleaved
+//     pieces, a fixed shared-memory tree, then the parts of a unit in index
+//     order (norm_partial_kernel + norm_finalize_kernel).
+// The scale 1/(||Y|| + eps) is folded into the first iteration's epilogues
+// instead of rewriting Y.
 #include "muon_device.h"
 #include "muon_internal.h"
 
