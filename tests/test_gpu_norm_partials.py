@@ -82,14 +82,14 @@ def test_momentum_sq_partials(ctx, gdt, udt, numel, offset):
     assert torch.equal(sq, sq2)
 
 
-def flat_update(ctx, shapes_counts, seed, pad=SQ_BLOCK):
-    """One flat bf16 update buffer (after `pad` leading elements) holding the
+def flat_update(ctx, shapes_counts, seed, pad=SQ_BLOCK, udt=torch.bfloat16):
+    """One flat update buffer (after `pad` leading elements) holding the
     matrices back to back, written by momentum_sq; returns views and partials."""
     total = pad + sum(r * c * n for (r, c), n in shapes_counts)
     g = gen(seed)
     grad = synth.normal((total,), 1e-3, g, DEV, torch.bfloat16)
     mom = synth.normal((total,), 1e-3, g, DEV, torch.float32)
-    upd = torch.empty(total, dtype=torch.bfloat16, device=DEV)
+    upd = torch.empty(total, dtype=udt, device=DEV)
     sq = torch.empty(sq_blocks(total), dtype=torch.float64, device=DEV)
     ctx.momentum_update(grad, mom, upd, 0.95, True, sq_partials=sq)
     groups = []
@@ -130,6 +130,25 @@ def test_ns_norms_from_partials(ctx, rows, cols, count, head_rows, method, fuse)
     # in the rare case of a sum on a rounding boundary
     assert d <= 1e-3
     assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("rows,cols,count,udt,tol", [
+    (512, 1024, 2, torch.float32, 1e-4),    # fp32 verification mode
+    (4096, 3, 4, torch.bfloat16, BF16_TOL),  # generic kernels (m = 3), three blocks per unit
+    (4096, 3, 4, torch.float32, 1e-4),
+])
+def test_ns_partials_other_paths(ctx, rows, cols, count, udt, tol):
+    upd, sq, (mats,) = flat_update(ctx, [((rows, cols), count)], seed=rows * cols + count, udt=udt)
+    p = ns_params(compute="bf16" if udt == torch.bfloat16 else "f32")
+    with_sq = [torch.empty_like(m) for m in mats]
+    plain = [torch.empty_like(m) for m in mats]
+    ctx.newton_schulz(mats, with_sq, 0, p, sq=(sq, upd))
+    ctx.newton_schulz(mats, plain, 0, p)
+    torch.cuda.synchronize()
+    d = max(oracle.rel_fro(host(a), host(b)) for a, b in zip(with_sq, plain))
+    err = max(oracle.rel_fro(host(o), oracle.ns_ref(host(m))) for o, m in zip(with_sq, mats))
+    say(f"  ns from partials {rows}x{cols} x{count} {udt}: vs norm pass {d:.2e}, vs oracle {err:.3e}")
+    assert d <= 1e-3 and err <= tol
 
 
 def test_ns_partials_in_place_and_tables(ctx):
