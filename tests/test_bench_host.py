@@ -1,0 +1,87 @@
+"""Host logic of bench.py (no GPU): flop accounting, unit lists, the refusal
+of more than one GPU.
+
+The algorithmic count per m x n unit (m <= n) and iteration is
+m(m+1)n (Gram, upper triangle) + m^2(m+1) (symmetric square) + 2m^2 n
+(update); the dense-equivalent count is 2m^2 n + 2m^3 + 2m^2 n.  The totals
+below are those closed forms summed by hand over each workload's shapes.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from newton_schulz_amd import synth  # noqa: E402
+
+
+def per_unit(m, n, steps=5):
+    return steps * (m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n)
+
+
+def dense_unit(m, n, steps=5):
+    return steps * (2 * m * m * n + 2 * m ** 3 + 2 * m * m * n)
+
+
+def totals(w):
+    units = bench.unit_list(w)
+    alg = sum(sum(bench.ns_flops(m, n, w.ns_steps)) for m, n in units)
+    dense = sum(dense_unit(m, n, w.ns_steps) for m, n in units)
+    return units, alg, dense
+
+
+def test_one_layer_counts():
+    units, alg, dense = totals(synth.qwen3_4b_layer())
+    # q, o -> (2560, 4096) x2; k, v -> (1024, 2560) x2; gate, up, down -> (2560, 9728) x3
+    assert sorted(units) == sorted([(2560, 4096)] * 2 + [(1024, 2560)] * 2 + [(2560, 9728)] * 3)
+    want = 2 * per_unit(2560, 4096) + 2 * per_unit(1024, 2560) + 3 * per_unit(2560, 9728)
+    assert alg == want
+    assert round(alg / 1e12, 3) == 4.186 and round(dense / 1e12, 3) == 5.867
+
+
+def test_full_model_counts():
+    w = synth.qwen3_4b()
+    units, alg, dense = totals(w)
+    assert len(w.mats) == 252 and len(units) == 252
+    assert sum(m.numel for m in w.mats) == 3633315840
+    assert round(alg / 1e12, 2) == 150.68 and round(dense / 1e12, 1) == 211.2
+
+
+def test_per_head_counts():
+    w = synth.qwen3_4b_heads()
+    units, alg, dense = totals(w)
+    assert len(units) == 1728 and set(units) == {(128, 2560)}
+    assert alg == 1728 * per_unit(128, 2560)
+    assert round(alg / 1e12, 3) == 1.108 and round(dense / 1e12, 3) == 1.486
+
+
+def test_expert_counts_skip_zero_experts():
+    w = synth.qwen3_30b_experts(layers=48)
+    units, alg, _ = totals(w)
+    assert len(w.mats) == 48 * 128 * 3
+    assert len(units) == len(w.mats) * 3 // 4        # 25% of experts carry zero gradients
+    assert set(units) == {(768, 2048)}
+    assert round(alg / 1e12, 1) == 281.9
+
+
+def test_tiny_counts():
+    units, alg, _ = totals(synth.tiny())
+    assert sorted(units) == sorted([(64, 128), (128, 128), (64, 256), (96, 96)])
+    assert alg == 86272000
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+@pytest.mark.parametrize("name", ["qwen3_4b", "qwen3_4b_layer", "qwen3_4b_heads",
+                                  "qwen3_30b_experts:2"])
+def test_workload_names(name):
+    assert bench.workload_by_name(name).mats
