@@ -85,3 +85,26 @@ def test_more_than_one_gpu_is_refused():
                                   "qwen3_30b_experts:2"])
 def test_workload_names(name):
     assert bench.workload_by_name(name).mats
+
+
+def read_golden(name):
+    vals = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", name)):
+        line = line.split("#")[0].strip()
+        if line:
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def test_qwen3_4b_muon_parameters_match_the_pages():
+    """The pages put Qwen3-4B's Muon momentum at 4 B per parameter, ~14.5 GB:
+    the 36-layer shape inventory (q, k, v, o, gate, up, down) must give that."""
+    g = read_golden("qwen3_4b_momentum_bytes.txt")
+    params = sum(m.numel for m in synth.qwen3_4b().mats)
+    assert round(params * g["bytes_per_param"] / 1e9, 1) == g["total_gb"]
+    # a plausible slip in the inventory (another FFN width, a missing layer,
+    # full-width k/v projections) lands elsewhere
+    assert round((params - 3 * 2560 * (9728 - 9216) * 36) * 4 / 1e9, 1) != g["total_gb"]
+    assert round(params * 35 / 36 * 4 / 1e9, 1) != g["total_gb"]
+    assert round((params + 2 * 2560 * (2560 - 1024) * 36) * 4 / 1e9, 1) != g["total_gb"]
