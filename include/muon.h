@@ -83,8 +83,8 @@ typedef enum { MUON_FUSE_AUTO = 0, MUON_FUSE_OFF = 1, MUON_FUSE_ON = 2 } muon_fu
 
 /* Newton-Schulz parameters.  The quintic iteration is the one the DeepSpeed
  * RFC "Enable Correct and High-Performance Muon Optimizer under ZeRO CPU
- * Offload" calls the current default (section 5, Roadmap), run for 5~6
- * iterations (section 2, Root Cause Analysis).  Per iteration, on the
+ * Offload" calls the current default (section 5, Roadmap), run for five to
+ * six iterations (section 2, Root Cause Analysis).  Per iteration, on the
  * normalised matrix X (m x n, m <= n):
  *     A = X X^T ;  B = b A + c A A ;  X <- a X + B X
  * (the library forms B' = a I + B and computes X <- B' X, the same product

@@ -14,10 +14,10 @@ section "Background: the conflict between FSDP and Muon":
 
 applied to whole 2D matrices (same page and section: orthogonalising shards
 separately is not the same as orthogonalising the full matrix), with the
-Newton-Schulz step being "the current quintic iteration" of the DeepSpeed RFC
-"Enable Correct and High-Performance Muon Optimizer under ZeRO CPU Offload",
-section 5 (Roadmap), run for 5 iterations (same RFC, section 2, Root Cause
-Analysis, says 5~6).  The pages print neither the polynomial's coefficients
+Newton-Schulz step being the quintic iteration that the DeepSpeed RFC
+"Enable Correct and High-Performance Muon Optimizer under ZeRO CPU Offload"
+names as its current one (section 5, Roadmap), run for 5 iterations (the
+same RFC, section 2, Root Cause Analysis, gives five to six).  The pages print neither the polynomial's coefficients
 nor the momentum formula; the readings taken here are:
 
   * momentum (EMA form, Nesterov):  M' = beta*M + (1-beta)*g,
