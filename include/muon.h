@@ -2,12 +2,12 @@
  * libmuon -- the Muon optimizer step's hot path on AMD Instinct MI355X (gfx950).
  *
  * The step, per whole 2D weight matrix (blog "Muon Optimizer + FSDP",
- * section "Background: the conflict between FSDP and Muon"):
- *
- *     M_t = momentum_update(grad)      -> muon_momentum_update (_sq: also the
- *                                         sums of squares for the norms)
- *     U_t = NewtonSchulz(M_t)          -> muon_newton_schulz_batched
- *     W_t = W_t - lr * U_t             -> muon_apply
+ * section "Background: the conflict between FSDP and Muon"), in three calls:
+ *   - refresh the momentum from the gradient   -> muon_momentum_update
+ *                                                 (_sq: also the sums of
+ *                                                 squares for the norms)
+ *   - orthogonalise it by Newton-Schulz        -> muon_newton_schulz_batched
+ *   - move the weight by -lr times the result  -> muon_apply
  *
  * Conventions shared by every entry point
  *   - Tensor arguments are DEVICE pointers to memory the caller owns and
@@ -239,7 +239,7 @@ void muon_plan_destroy(muon_plan_t* plan);
 /* ------------------------------------------------------------------------ */
 
 /* Momentum with Nesterov look-ahead over `numel` contiguous elements
- * (blog, section "Background": M_t = momentum_update(grad); RFC section 2:
+ * (blog, section "Background": the momentum refresh; RFC section 2:
  * the first-order momentum the offload path must keep).  Per element, each
  * operation one IEEE binary32 rounding, no fused multiply-add:
  *     t  = (1 - beta) * g
@@ -293,7 +293,8 @@ muon_status_t muon_newton_schulz_batched(muon_ctx_t* ctx, void* stream, const vo
                                          int* nonfinite_flag);
 
 /* Weight apply over `numel` contiguous elements (blog, section "Background":
- * W_t = W_t - lr * U_t).  Each operation one binary32 rounding, no FMA:
+ * the weight moves by -lr times the orthogonalised update).  Each
+ * operation one binary32 rounding, no FMA:
  *     eta = lr * scale;  W1 = W * (1 - lr * weight_decay) if weight_decay != 0
  *     W'  = W1 - eta * u                        (written back to master)
  *     weight_bf16 = W' rounded to nearest-even  (when weight_bf16 != NULL)

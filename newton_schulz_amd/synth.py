@@ -155,3 +155,53 @@ def draw_grads(w: Workload, gen: torch.Generator, device, out: Optional[List[tor
 
 def draw_weights(w: Workload, gen: torch.Generator, device):
     return [normal((m.rows, m.cols), w.weight_std, gen, device, torch.float32) for m in w.mats]
+
+
+# Spectra that Gaussian draws do not reach.  Newton-Schulz lifts every
+# singular value towards 1, small ones by up to a^steps, so inputs whose
+# spectrum spans many orders of magnitude exercise precision that an i.i.d.
+# Gaussian matrix (singular values within about one order) does not.
+STRUCTURED_KINDS = ("gauss", "rank1", "rank8_noise", "geometric")
+
+
+def structured(kind: str, rows: int, cols: int, seed: int, std: float = 1e-3,
+               scale: float = 1.0, device=None, dtype=torch.bfloat16) -> torch.Tensor:
+    """A seeded rows x cols matrix with a chosen spectrum, drawn on the host in
+    float64 (torch CPU generator, so the values do not depend on the device),
+    multiplied by `scale`, cast to `dtype` (round to nearest even) and moved
+    to `device`.
+
+      gauss        i.i.d. N(0, std)
+      rank1        std * u v^T, u and v i.i.d. N(0, 1)
+      rank8_noise  std * L R / sqrt(8) (L rows x 8, R 8 x cols, N(0, 1)) plus
+                   i.i.d. N(0, 1e-3 std) noise: eight large singular values
+                   over a floor about 1e-3 below them
+      geometric    std * Q1 diag(sigma) Q2^T with Haar-random orthonormal Q1,
+                   Q2 (QR of Gaussian draws, signs fixed by R's diagonal) and
+                   sigma_i = 10^(-6 i / (k - 1)), k = min(rows, cols): a
+                   geometric spectrum over six decades
+    """
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    f64 = torch.float64
+    if kind == "gauss":
+        y = torch.randn(rows, cols, generator=g, dtype=f64) * std
+    elif kind == "rank1":
+        y = torch.outer(torch.randn(rows, generator=g, dtype=f64),
+                        torch.randn(cols, generator=g, dtype=f64)) * std
+    elif kind == "rank8_noise":
+        L = torch.randn(rows, 8, generator=g, dtype=f64)
+        R = torch.randn(8, cols, generator=g, dtype=f64)
+        y = (L @ R) * (std / 8 ** 0.5) + torch.randn(rows, cols, generator=g, dtype=f64) * (1e-3 * std)
+    elif kind == "geometric":
+        k = min(rows, cols)
+
+        def haar(n, p):
+            q, r = torch.linalg.qr(torch.randn(n, p, generator=g, dtype=f64))
+            return q * torch.sign(torch.diagonal(r))
+
+        sig = 10.0 ** (-6.0 * torch.arange(k, dtype=f64) / max(k - 1, 1))
+        y = (haar(rows, k) * sig) @ haar(cols, k).T * std
+    else:
+        raise ValueError(f"unknown spectrum kind {kind!r}")
+    y = (y * scale).to(torch.float32).to(dtype)
+    return y.to(device) if device is not None else y

@@ -6,13 +6,10 @@ benchmark's CPU-baseline leg may import it; the product path never calls it
 and shares no code with it (no kernels, headers, helpers or tables).
 
 What it computes follows the update rule of the blog "Muon Optimizer + FSDP",
-section "Background: the conflict between FSDP and Muon":
-
-    M_t = momentum_update(grad)
-    U_t = NewtonSchulz(M_t)
-    W_t = W_t - lr * U_t
-
-applied to whole 2D matrices (same page and section: orthogonalising shards
+section "Background: the conflict between FSDP and Muon": the gradient first
+refreshes a momentum buffer, the momentum is orthogonalised by Newton-Schulz,
+and the weight moves against that orthogonalised update scaled by the
+learning rate -- applied to whole 2D matrices (same page and section: orthogonalising shards
 separately is not the same as orthogonalising the full matrix), with the
 Newton-Schulz step being the quintic iteration that the DeepSpeed RFC
 "Enable Correct and High-Performance Muon Optimizer under ZeRO CPU Offload"
@@ -98,8 +95,8 @@ def bf16_from_bits(bits) -> np.ndarray:
 def momentum_ref(g, M, beta: float = 0.95, nesterov: bool = True):
     """One momentum update per element; returns (M_new, U_in), both float32.
 
-    Follows M_t = momentum_update(grad) of the blog's Background section, in
-    EMA form with Nesterov look-ahead.  Operation order (each step one
+    The momentum refresh of the blog's Background section, read as an
+    exponential moving average with Nesterov look-ahead.  Operation order (each step one
     binary32 rounding):  c1 = 1 - beta;  t = c1*g;  M' = beta*M + t;
     U_in = t + beta*M'  (or U_in = M' without Nesterov).
     """
@@ -298,8 +295,9 @@ def apply_ref(W, u, lr: float, scale: float = 1.0, weight_decay: float = 0.0,
               bf16_copy: bool = False):
     """W' = W1 - (lr*scale)*u with W1 = W*(1 - lr*wd) when wd != 0.
 
-    The blog's Background section writes the apply as W_t = W_t - lr * U_t;
-    `scale` and `weight_decay` default to 1 and 0.  Each operation is one
+    The blog's Background section moves the weight against the orthogonalised
+    update times the learning rate; `scale` and `weight_decay` default to 1
+    and 0.  Each operation is one
     binary32 rounding.  Returns W' (float32) and, when asked, the bf16 bit
     patterns of W' rounded to nearest-even.
     """
