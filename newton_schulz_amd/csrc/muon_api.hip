@@ -465,6 +465,9 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   float* scale = reinterpret_cast<float*>(ws + L.scale);
   int* zflag = reinterpret_cast<int*>(ws + L.zflag);
   double* partial = reinterpret_cast<double*>(ws + L.partial);
+  // BF16 compute carries the iterate past bf16: residual plane and B's diagonal
+  char* lo_plane = prm->compute == MUON_BF16 ? ws + L.lo : nullptr;
+  float* dvec = prm->compute == MUON_BF16 ? reinterpret_cast<float*>(ws + L.dvec) : nullptr;
   const int io_bf16 = io_dtype == MUON_BF16;
   const bool tall = L.ur > L.uc;
   const int64_t m = L.m, n = L.n;
@@ -564,6 +567,8 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     fa.scale = scale;
     fa.zflag = zflag;
     // a fixed triple is one row that every iteration reuses
+    fa.dvec = dvec;
+    fa.lo = lo_plane;
     fa.ncoef = prm->coeffs ? prm->steps : 1;
     for (int k = 0; k < fa.ncoef; ++k) coef(k, &fa.coef[k][0], &fa.coef[k][1], &fa.coef[k][2]);
     const long k = tstart(c, s, MUON_K_FUSED);
@@ -669,6 +674,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     sa.pm = AR; sa.pn = AR; sa.dst = BR; sa.epi = AR;
     sa.ldm = sa.ldn = sa.ldd = sa.lde = m;
     sa.M = sa.N = sa.K = static_cast<int>(m);
+    sa.dvec = dvec;
     coef(k, &sa.ca, &sa.cb, &sa.cc);
     e = gemm(MUON_K_SYMSQ, sa, EPI_SYMSQ, false, false);
     if (e != hipSuccess) return hip_fail(c, e, "symsq launch");
@@ -678,6 +684,14 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     ua.scale = scale;
     ua.scale_pow = (k == 0) ? 1 : 0;
     ua.zero_write = last ? 1 : 0;
+    // B's diagonal completed in fp32 and the residual carried from update to
+    // update (read and rewritten tile by tile, in place); the generic kernel
+    // reads the iterate at the output position through epi
+    ua.dvec = dvec;
+    ua.epi = src;
+    ua.lde = tall ? m : n;
+    ua.lo_in = (k == 0 || lo_plane == nullptr) ? nullptr : lo_plane;
+    ua.lo_out = last ? nullptr : lo_plane;
     if (!tall) {
       // X' = B' X : rows from B', columns from X (K-major)
       ua.pm = BR; ua.ldm = m;

@@ -28,6 +28,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 template <typename T> struct Elem;
+
+// fp32 -> the nearest bf16 value, as fp32.
+__device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+// The bf16 iteration with the iterate carried past bf16.  The iterate is
+// X = hi + lo: hi the stored bf16 matrix the products read, lo its rounding
+// residual (kept in a plane of its own).  The MFMA applies B' with its
+// diagonal d rounded to bf16, so it sums (B'_bf16 hi)_ij; the diagonal's exact
+// contribution d X_ij = bf16(d) hi + (d - bf16(d)) hi + d lo is completed in
+// fp32: r hi (r = ns_diag_residual(d)) is added to the accumulator just
+// before the MFMAs of the k-stage holding row i (wide; column j when tall),
+// d lo after the last one (ns_lo_term).  Without this, the small singular
+// values that the iteration lifts by up to a^steps are lost in the bf16
+// storage of X.  Every kernel computing it keeps this order (no contraction),
+// so they give the same bits.
+__device__ __forceinline__ float ns_diag_residual(float d) { return d - bf16_round(d); }
+__device__ __forceinline__ float ns_lo_term(float acc, float d, float lo) { return acc + d * lo; }
+
 template <> struct Elem<float> {
   static __device__ __forceinline__ float load(const float* p) { return *p; }
   static __device__ __forceinline__ void store(float* p, float v) { *p = v; }

@@ -32,6 +32,18 @@ struct NsGemmArgs {
   const int* zflag;    // per-unit "norm is zero" flag, or nullptr
   int zero_write;      // EPI_UPDATE: write zeros for zero units (last iteration)
   float ca, cb, cc;    // quintic coefficients a, b, c
+  // Iterate carried past bf16 (ns_diag_residual, ns_lo_term).  EPI_SYMSQ:
+  // dvec, when set, receives B's diagonal in fp32 before rounding (K floats
+  // per unit, unit u at u * K).  EPI_UPDATE: dvec set = complete the
+  // diagonal (the MFMA kernel reads the iterate at the output position from
+  // its own k-stages, the generic kernel through epi / lde); lo_in = the
+  // input's residual plane (nullptr: the input is exact in bf16), lo_out =
+  // receives the output's residual (nullptr: not kept).  The MFMA kernel
+  // keeps residuals in its own tile-major order (tile lid at lid * BM * BN *
+  // 2 bytes, each lane's values contiguous); the generic kernel row-major.
+  float* dvec;
+  const char* lo_in;
+  char* lo_out;
 };
 
 struct NsNormArgs {
@@ -63,6 +75,8 @@ struct NsSmallArgs {
   int64_t units;
   const float* scale;  // per-unit s = 1 / (||Y||_F + eps)
   const int* zflag;    // per-unit "norm is zero" flag, or nullptr
+  float* dvec;         // quintic: B's fp32 diagonal, m floats per unit
+  char* lo;            // quintic: residual planes, nb 32 KiB blocks per unit
   int ncoef;           // rows of coef: iteration k uses row min(k, ncoef - 1)
   float coef[MUON_NS_FUSED_MAX_ROWS][3];  // (a, b, c) per iteration
 };

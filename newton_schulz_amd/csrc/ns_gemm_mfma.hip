@@ -172,6 +172,11 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   __shared__ __attribute__((aligned(1024))) char st1[STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[NS > 2 ? STAGE : 16];
   __shared__ __attribute__((aligned(1024))) char st3[NS > 2 ? STAGE : 16];
+  // corrected update: bf16(r), r = d - bf16(d), and d along the tile's
+  // diagonal side
+  constexpr int DS = EPI == EPI_UPDATE ? (TN ? BM : BN) : 1;
+  __shared__ uint16_t corr_r[DS];
+  __shared__ float corr_d[DS];
   auto buf = [&](auto I) -> char* {
     constexpr int i = decltype(I)::value % NS;
     if constexpr (i == 0) return st0;
@@ -231,6 +236,23 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = (f32x16_t)(0.0f);
 
+  // update with the iterate carried past bf16 (ns_diag_residual): B's fp32
+  // diagonal along the output's rows (wide, X' = B'X) or columns (tall,
+  // Y' = YB').  Not for a zero unit: it writes zeros and its workspace was
+  // never filled.
+  const bool corr = EPI == EPI_UPDATE && a.dvec != nullptr && !zero_unit;
+  const int64_t dbase = u * static_cast<int64_t>(a.K);
+  if (corr) {
+    const int d0 = TN ? m0 : n0, dlim = TN ? a.M : a.N;
+    for (int i = tid; i < DS; i += NT) {
+      const float d = d0 + i < dlim ? a.dvec[dbase + d0 + i] : 0.0f;
+      corr_d[i] = d;
+      corr_r[i] = muon::f32_to_bf16(muon::ns_diag_residual(d));
+    }
+    // visible to every wave at the k-loop's first barrier
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  }
+
   if (!zero_unit) {
     using OpM = Operand<BM, TM, NW, BK>;
     using OpN = Operand<BN, TN, NW, BK>;
@@ -286,9 +308,61 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
     // (the NS - 2 later stages may still fly) and this wave's reads of stage
     // kt are done; the barrier then makes stage kt + 1 visible and frees
     // buffer kt % NS, which receives stage kt + NS.
+    // The diagonal's residual r (in bf16) as a matrix-core operand: for k16
+    // step kk of stage kt, whose 16 k-indices are the output rows (wide,
+    // X' = B'X) or columns (tall, Y' = YB') k16 .. k16 + 15 of this tile,
+    // the 32 x 16 slice of diag(r) meets the step's X (Y) fragment in one
+    // more MFMA per accumulator of that 32-block: acc += r hi, exactly, with
+    // no vector-ALU write to the accumulators inside the loop.  A lane's
+    // slice row holds at most one nonzero k.
+    auto diag_frag = [&](int idx, int k16) __attribute__((always_inline)) {
+      const int e = idx - k16 - 8 * (lane >> 5);  // which of the lane's 8 k is idx
+      const uint32_t rb = (e >= 0 && e < 8) ? static_cast<uint32_t>(corr_r[idx]) : 0u;
+      const uint32_t w = (e & 1) ? (rb << 16) : rb;
+      const int q = e >> 1;
+      const u32x4_t v = {q == 0 ? w : 0u, q == 1 ? w : 0u, q == 2 ? w : 0u, q == 3 ? w : 0u};
+      return __builtin_bit_cast(bf16x8_t, v);
+    };
+    auto diag_mfmas = [&](int kt, auto KI, auto BUF) __attribute__((always_inline)) {
+      constexpr int kk = decltype(KI)::value, b = decltype(BUF)::value;
+      const int k16 = kt * BK + 16 * kk - (TN ? m0 : n0);
+      if constexpr (TN) {
+        // rows k16 .. k16 + 15: wave row wm = k16 / WM, block (k16 % WM) / 32
+        if (corr && k16 >= 0 && k16 < BM && k16 / WM == wm) {
+          const int mis = (k16 % WM) / 32;
+          const bf16x8_t fd = diag_frag(wm * WM + mis * 32 + (lane & 31), k16);
+          static_for<FM>([&](auto MI) __attribute__((always_inline)) {
+            constexpr int mi = decltype(MI)::value;
+            if (mi == mis) {
+              static_for<FN>([&](auto NI) __attribute__((always_inline)) {
+                constexpr int ni = decltype(NI)::value;
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[b][ni], fd, acc[mi][ni], 0, 0, 0);
+              });
+            }
+          });
+        }
+      } else {
+        // columns k16 .. k16 + 15: wave column wn = k16 / WN, block (k16 % WN) / 32
+        if (corr && k16 >= 0 && k16 < BN && k16 / WN == wn) {
+          const int nis = (k16 % WN) / 32;
+          const bf16x8_t fd = diag_frag(wn * WN + nis * 32 + (lane & 31), k16);
+          static_for<FN>([&](auto NI) __attribute__((always_inline)) {
+            constexpr int ni = decltype(NI)::value;
+            if (ni == nis) {
+              static_for<FM>([&](auto MI) __attribute__((always_inline)) {
+                constexpr int mi = decltype(MI)::value;
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fd, fb[b][mi], acc[mi][ni], 0, 0, 0);
+              });
+            }
+          });
+        }
+      }
+    };
+
     auto stage = [&](auto S, int kt_new) {
       char* cur = buf(S);
       const char* nxt = buf(ic<decltype(S)::value + 1>{});
+      const int kt_cur = kt_new - NS;
       static_for<KK>([&](auto KI) {
         constexpr int kk = decltype(KI)::value;
         constexpr int b = kk & 1;
@@ -297,6 +371,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
           mfmas(ic<b>{}, ic<0>{}, ic<NMF>{});
           interleave(ic<NMF>{});
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (EPI == EPI_UPDATE) diag_mfmas(kt_cur, ic<kk>{}, ic<b>{});
         } else {
           mfmas(ic<b>{}, ic<0>{}, ic<NMF - TAIL>{});
           __builtin_amdgcn_sched_barrier(0);
@@ -309,6 +384,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
           mfmas(ic<b>{}, ic<NMF - TAIL>{}, ic<NMF>{});
           interleave(ic<TAIL>{});
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (EPI == EPI_UPDATE) diag_mfmas(kt_cur, ic<kk>{}, ic<b>{});
         }
       });
     };
@@ -379,9 +455,25 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 15));
     __syncthreads();
   }
+  // Residual planes are tile-major: lane l of wave w keeps its values of the
+  // 32-row block mi, columns ni 32 + 16 h .. (h = 0, 1: two register groups
+  // g = 2 h, 2 h + 1) as 16-byte chunk (mi 2 FN + 2 ni + h) of the tile, at
+  // chunk * NW KiB + w KiB + 16 l: whole-wave, contiguous 1 KiB accesses.
+  constexpr int TILE_LO = BM * BN * 2;
+  auto lo_chunk = [&](const char* plane, int ch) {
+    return plane + lid * TILE_LO + (ch * NW + wave) * 1024 + elane * 16;
+  };
   static_for<FM>([&](auto MI) {
     constexpr int mi = decltype(MI)::value;
     const int il = wm * WM + mi * 32 + (elane & 31);
+    u32x4_t lov[2 * FN];   // input residuals of this 32-row block
+    u32x4_t lon[2 * FN];   // output residuals
+    const bool use_lo = corr && a.lo_in != nullptr;
+    if (use_lo) {
+#pragma unroll
+      for (int ch = 0; ch < 2 * FN; ++ch)
+        lov[ch] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(lo_chunk(a.lo_in, mi * 2 * FN + ch)));
+    }
     static_for<FN>([&](auto NI) {
       constexpr int ni = decltype(NI)::value;
       static_for<4>([&](auto G) {
@@ -391,9 +483,38 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
                       acc[mi][ni][4 * g + 3]};
         uint2* slot = reinterpret_cast<uint2*>(ct.at(il, jl));
         if (EPI != EPI_SYMSQ) {
+          if (use_lo) {
+            // + d lo: d per row (wide, X' = B'X) or per column (tall, Y' = YB')
+            const u32x4_t lc = lov[2 * ni + g / 2];
+            const uint32_t l0 = (g & 1) ? lc.z : lc.x, l1 = (g & 1) ? lc.w : lc.y;
+            const float lo[4] = {__uint_as_float(l0 << 16), __uint_as_float(l0 & 0xffff0000u),
+                                 __uint_as_float(l1 << 16), __uint_as_float(l1 & 0xffff0000u)};
+            float d[4];
+            if (TN) {
+              d[0] = d[1] = d[2] = d[3] = corr_d[il];
+            } else {
+              const float4 dv = *reinterpret_cast<const float4*>(corr_d + jl);
+              d[0] = dv.x; d[1] = dv.y; d[2] = dv.z; d[3] = dv.w;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = muon::ns_lo_term(v[q], d[q], lo[q]);
+          }
           const float f = zero_unit ? 0.0f : s;  // a zero unit's update writes zeros
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = f * v[q];
+          if (corr) {
+            float r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r[q] = v[q] - muon::bf16_round(v[q]);
+            u32x4_t& lo_out = lon[2 * ni + g / 2];
+            if (g & 1) {
+              lo_out.z = muon::pack_bf16x2(r[0], r[1]);
+              lo_out.w = muon::pack_bf16x2(r[2], r[3]);
+            } else {
+              lo_out.x = muon::pack_bf16x2(r[0], r[1]);
+              lo_out.y = muon::pack_bf16x2(r[2], r[3]);
+            }
+          }
         } else {
           const uint2 w = *slot;
           const float e[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
@@ -401,7 +522,11 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             v[q] = a.cb * e[q] + a.cc * v[q];
-            if (diag_tile && il == jl + q) v[q] += a.ca;
+            if (diag_tile && il == jl + q) {
+              v[q] += a.ca;
+              // B's diagonal before rounding, for the update's correction
+              if (a.dvec != nullptr && m0 + il < a.M) a.dvec[u * static_cast<int64_t>(a.M) + m0 + il] = v[q];
+            }
           }
         }
         uint2 w;
@@ -413,6 +538,12 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
       // hoisted all together (register pressure)
       __builtin_amdgcn_sched_barrier(0);
     });
+    if (corr && a.lo_out) {
+#pragma unroll
+      for (int ch = 0; ch < 2 * FN; ++ch)
+        __builtin_nontemporal_store(lon[ch], reinterpret_cast<u32x4_t*>(
+                                                 const_cast<char*>(lo_chunk(a.lo_out, mi * 2 * FN + ch))));
+    }
   });
   __syncthreads();
 

@@ -1,7 +1,15 @@
 // Generic Newton-Schulz products for any shape: the fp32 verification mode
 // and bf16 shapes the MFMA path does not take (a dimension not a multiple of
 // 8, or unaligned bases).  Same products, epilogues and rounding points as
-// the MFMA path; fp32 fused multiply-add accumulation, 64 x 64 tiles, BK 16.
+// the MFMA path; 64 x 64 tiles, BK 16, fused multiply-add accumulation.
+// bf16 storage accumulates in fp32 (as the matrix cores do).  The fp32 mode
+// stores every matrix in fp32 but accumulates and finishes each product in
+// fp64: the iteration lifts singular values near the storage precision by up
+// to a^steps, and with fp32 sums over fp32 data nothing is left to resolve
+// them (an exactly rank-1 fp32 input then misses 1e-4 relative error; with
+// fp64 sums it stays near 4e-6).
+#include <type_traits>
+
 #include "muon_device.h"
 #include "muon_internal.h"
 
@@ -31,8 +39,14 @@ __device__ __forceinline__ void stage(float (*sh)[TS + 4], const T* __restrict__
   }
 }
 
+__device__ __forceinline__ float fma_acc(float x, float y, float c) { return __builtin_fmaf(x, y, c); }
+__device__ __forceinline__ double fma_acc(float x, float y, double c) {
+  return __builtin_fma(static_cast<double>(x), static_cast<double>(y), c);
+}
+
 template <typename T, bool TM, bool TN, int EPI>
 __global__ __launch_bounds__(256) void ns_gemm_simple_kernel(NsGemmArgs a) {
+  using Acc = std::conditional_t<std::is_same<T, float>::value, double, float>;
   __shared__ float sM[BKS][TS + 4];
   __shared__ float sN[BKS][TS + 4];
   const int tid = threadIdx.x;
@@ -51,11 +65,11 @@ __global__ __launch_bounds__(256) void ns_gemm_simple_kernel(NsGemmArgs a) {
   if (zero_unit && !(EPI == EPI_UPDATE && a.zero_write)) return;
 
   const int ty = tid / 16, tx = tid % 16;
-  float acc[4][4];
+  Acc acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+    for (int j = 0; j < 4; ++j) acc[i][j] = Acc(0);
 
   if (!zero_unit) {
     const T* pm = reinterpret_cast<const T*>(mat_at(a.pm, u));
@@ -74,19 +88,26 @@ __global__ __launch_bounds__(256) void ns_gemm_simple_kernel(NsGemmArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(x[i], y[j], acc[i][j]);
+          for (int j = 0; j < 4; ++j) acc[i][j] = fma_acc(x[i], y[j], acc[i][j]);
       }
       __syncthreads();
     }
   }
 
-  float s = 1.0f;
+  Acc s = Acc(1);
   if (a.scale != nullptr && a.scale_pow > 0) {
     s = a.scale[u];
     if (a.scale_pow == 2) s = s * s;
   }
   T* dst = reinterpret_cast<T*>(mat_at(a.dst, u));
-  const T* ep = (EPI == EPI_SYMSQ) ? reinterpret_cast<const T*>(mat_at(a.epi, u)) : nullptr;
+  // the corrected bf16 update (ns_diag_residual, ns_lo_term) reads the source at the
+  // output position through epi and keeps its residual row-major, M x N per
+  // unit; never for a zero unit (its workspace was never filled)
+  const bool corr = EPI == EPI_UPDATE && a.dvec != nullptr && !zero_unit;
+  const T* ep = (EPI == EPI_SYMSQ || corr) ? reinterpret_cast<const T*>(mat_at(a.epi, u)) : nullptr;
+  const int64_t plane = u * static_cast<int64_t>(a.M) * a.N;
+  const bf16_t* lo_in = reinterpret_cast<const bf16_t*>(a.lo_in);
+  bf16_t* lo_out = reinterpret_cast<bf16_t*>(a.lo_out);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int gi = m0 + ty * 4 + i;
@@ -95,20 +116,37 @@ __global__ __launch_bounds__(256) void ns_gemm_simple_kernel(NsGemmArgs a) {
     for (int j = 0; j < 4; ++j) {
       const int gj = n0 + tx * 4 + j;
       if (gj >= a.N) continue;
-      float v = acc[i][j];
+      Acc v = acc[i][j];
       if (EPI == EPI_GRAM) {
         v = s * v;
       } else if (EPI == EPI_SYMSQ) {
-        v = a.cb * muon::Elem<T>::load(ep + static_cast<int64_t>(gi) * a.lde + gj) + a.cc * v;
-        if (gi == gj) v += a.ca;
+        v = Acc(a.cb) * Acc(muon::Elem<T>::load(ep + static_cast<int64_t>(gi) * a.lde + gj)) + Acc(a.cc) * v;
+        if (gi == gj) {
+          v += Acc(a.ca);
+          if (a.dvec != nullptr) a.dvec[u * static_cast<int64_t>(a.M) + gi] = static_cast<float>(v);
+        }
       } else {
-        v = zero_unit ? 0.0f : s * v;
+        if (corr) {
+          // d per row for X' = B'X (the K-major X operand), per column for Y' = YB'
+          const float d = a.dvec[u * static_cast<int64_t>(a.K) + (TN ? gi : gj)];
+          const float hi = muon::Elem<T>::load(ep + static_cast<int64_t>(gi) * a.lde + gj);
+          const int64_t e = plane + static_cast<int64_t>(gi) * a.N + gj;
+          const float lo = lo_in ? muon::bf16_to_f32(lo_in[e]) : 0.0f;
+          float w = static_cast<float>(v) + muon::ns_diag_residual(d) * hi;
+          if (lo_in) w = muon::ns_lo_term(w, d, lo);
+          v = w;
+        }
+        v = zero_unit ? Acc(0) : s * v;
+        if (corr && lo_out) {
+          const float f = static_cast<float>(v);
+          lo_out[plane + static_cast<int64_t>(gi) * a.N + gj] = muon::f32_to_bf16(f - muon::bf16_round(f));
+        }
       }
       if (EPI == EPI_UPDATE) {
-        muon::Elem<T>::store(dst + static_cast<int64_t>(gi) * a.ldd + gj, v);
+        muon::Elem<T>::store(dst + static_cast<int64_t>(gi) * a.ldd + gj, static_cast<float>(v));
       } else if (ti != tj || gi <= gj) {
-        muon::Elem<T>::store(dst + static_cast<int64_t>(gi) * a.ldd + gj, v);
-        muon::Elem<T>::store(dst + static_cast<int64_t>(gj) * a.ldd + gi, v);
+        muon::Elem<T>::store(dst + static_cast<int64_t>(gi) * a.ldd + gj, static_cast<float>(v));
+        muon::Elem<T>::store(dst + static_cast<int64_t>(gj) * a.ldd + gi, static_cast<float>(v));
       }
     }
   }

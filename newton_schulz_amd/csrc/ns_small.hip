@@ -230,8 +230,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     mirror_lower(d, tid);
     barrier_lds();
   };
-  // d = a I + b A + c A A (A in am) with iteration k's coefficients
-  auto symsq = [&](char* d, int k) {
+  // d = a I + b A + c A A (A in am) with iteration k's coefficients; with
+  // dg set, the diagonal before rounding also goes to dg[0 .. m) (global: the
+  // on-chip memory is taken), visible to the whole workgroup after the
+  // barrier
+  auto symsq = [&](char* d, int k, float* dg) {
     const int r = k < a.ncoef ? k : a.ncoef - 1;
     const float ca = a.coef[r][0], cb = a.coef[r][1], cc = a.coef[r][2];
     Acc acc;
@@ -244,17 +247,39 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[q] = cb * e[q] + cc * acc.v[mi][ni][4 * g + q];
-        if (i == j + q) v[q] += ca;
+        if (i == j + q) {
+          v[q] += ca;
+          if (dg != nullptr && i < m) dg[i] = v[q];
+        }
       }
       *reinterpret_cast<uint2*>(rt_at(d, i, j)) = pack4(v);
     });
+    if (dg != nullptr) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     barrier_lds();
     mirror_lower(d, tid);
     barrier_lds();
   };
   // xd = f B xs (B in bp) block by block through the staging tile am; with
-  // `next`, an accumulates xd xd^T from the stored bf16 blocks
-  auto column_pass = [&](const bf16_t* xs, const bf16_t* xd, float f, bool next, Acc& an) {
+  // `next`, an accumulates xd xd^T from the stored bf16 blocks.  With dg set
+  // (quintic), B's fp32 diagonal is completed and the iterate's residual
+  // carried (ns_diag_residual, ns_lo_term): lo_in / lo_out are the unit's residual planes
+  // (one 32 KiB block per column block, each lane's values of a 32-row block
+  // as four contiguous chunks; lo_in null for the exact bf16 input, lo_out
+  // null when not kept).
+  auto column_pass = [&](const bf16_t* xs, const bf16_t* xd, float f, bool next, Acc& an,
+                         const float* dg, const char* lo_in, char* lo_out) {
+    float drow[2] = {0.0f, 0.0f};
+    if (dg != nullptr) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int i = wm * 64 + mi * 32 + (lane & 31);
+        if (i < m) drow[mi] = dg[i];
+      }
+    }
+    auto lo_chunk = [&](const char* plane, int c, int ch) {
+      return const_cast<char*>(plane) + static_cast<int64_t>(c) * SLAB + (ch * NWV + wave) * 1024 +
+             lane * 16;
+    };
     const u32x4_t rs = rsrc_words(xs, ubytes);
     uint32_t base[NGC];
     int cc[NGC];
@@ -278,8 +303,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     for (int c = 0; c < nb; ++c) {
       char* sl = (c % 3 == 0) ? s0 : ((c % 3 == 1) ? s1 : s2);
       // wait for this wave's block-c loads; issued after them: blocks c + 1,
-      // c + 2 (8 loads each) and the stores of blocks c - 2, c - 1 (8 each)
-      if (c == 0)
+      // c + 2 (8 loads each) and the stores of blocks c - 2, c - 1 (8 each).
+      // With the residual, the loads and stores of the residual blocks come
+      // in between too: wait for everything (the count would depend on the
+      // residual's presence; this path is not the bandwidth-critical one).
+      if (dg != nullptr)
+        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (c == 0)
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC) : "memory");
       else if (c == 1)
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC + NST) : "memory");
@@ -296,13 +326,80 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
           fb[i] = rt_frag(bp, wm * 64 + i * 32, kk, lane);
         }
         ax.mma(fa, fb);
+        // B's diagonal residual r (bf16) on the 16 rows this step contracts
+        // over, as one more MFMA per accumulator of their 32-row block: the
+        // same operand and order as the 128-tile launches
+        if (dg != nullptr && (kk >> 2) == wm) {
+          const int mis = (kk >> 1) & 1;
+          const int idx = wm * 64 + mis * 32 + (lane & 31);
+          const int e = idx - 16 * kk - 8 * (lane >> 5);
+          const uint32_t rb = (e >= 0 && e < 8)
+                                  ? static_cast<uint32_t>(muon::f32_to_bf16(muon::ns_diag_residual(drow[mis])))
+                                  : 0u;
+          const uint32_t w = (e & 1) ? (rb << 16) : rb;
+          const int q = e >> 1;
+          const u32x4_t v = {q == 0 ? w : 0u, q == 1 ? w : 0u, q == 2 ? w : 0u, q == 3 ? w : 0u};
+          const bf16x8_t fd = __builtin_bit_cast(bf16x8_t, v);
+          if (mis == 0) {
+            ax.v[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fd, ax.v[0][0], 0, 0, 0);
+            ax.v[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fd, ax.v[0][1], 0, 0, 0);
+          } else {
+            ax.v[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fd, ax.v[1][0], 0, 0, 0);
+            ax.v[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fd, ax.v[1][1], 0, 0, 0);
+          }
+        }
       }
-      for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
-        float v[4];
+      if (dg == nullptr) {
+        for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
+          float v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = f * ax.v[mi][ni][4 * g + q];
-        *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
-      });
+          for (int q = 0; q < 4; ++q) v[q] = f * ax.v[mi][ni][4 * g + q];
+          *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
+        });
+      } else {
+        static_for<2>([&](auto MI) {
+          constexpr int mi = decltype(MI)::value;
+          u32x4_t lov[4], lon[4];
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch)
+            lov[ch] = lo_in ? __builtin_nontemporal_load(
+                                  reinterpret_cast<const u32x4_t*>(lo_chunk(lo_in, c, mi * 4 + ch)))
+                            : u32x4_t{0u, 0u, 0u, 0u};
+          static_for<2>([&](auto NI) {
+            static_for<4>([&](auto G) {
+              constexpr int ni = decltype(NI)::value, g = decltype(G)::value;
+              const int i = wm * 64 + mi * 32 + (lane & 31);
+              const int j = wn * 64 + ni * 32 + 8 * g + 4 * (lane >> 5);
+              const u32x4_t lc = lov[2 * ni + g / 2];
+              const uint32_t l0 = (g & 1) ? lc.z : lc.x, l1 = (g & 1) ? lc.w : lc.y;
+              const float lo[4] = {__uint_as_float(l0 << 16), __uint_as_float(l0 & 0xffff0000u),
+                                   __uint_as_float(l1 << 16), __uint_as_float(l1 & 0xffff0000u)};
+              float v[4], r[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] = ax.v[mi][ni][4 * g + q];
+                if (lo_in) v[q] = muon::ns_lo_term(v[q], drow[mi], lo[q]);
+                v[q] = f * v[q];
+                r[q] = v[q] - muon::bf16_round(v[q]);
+              }
+              u32x4_t& lw = lon[2 * ni + g / 2];
+              if (g & 1) {
+                lw.z = muon::pack_bf16x2(r[0], r[1]);
+                lw.w = muon::pack_bf16x2(r[2], r[3]);
+              } else {
+                lw.x = muon::pack_bf16x2(r[0], r[1]);
+                lw.y = muon::pack_bf16x2(r[2], r[3]);
+              }
+              *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
+            });
+          });
+          if (lo_out) {
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch)
+              __builtin_nontemporal_store(lon[ch], reinterpret_cast<u32x4_t*>(lo_chunk(lo_out, c, mi * 4 + ch)));
+          }
+        });
+      }
       barrier_lds();
       store_block(xd, c * SM, am);
       if (next) {
@@ -325,15 +422,19 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
   };
 
   if constexpr (!GRAM) {
+    // B's fp32 diagonal and the residual planes of this unit
+    float* dg = a.dvec ? a.dvec + u * static_cast<int64_t>(m) : nullptr;
+    char* lo = a.lo ? a.lo + u * static_cast<int64_t>(nb) * SLAB : nullptr;
     for (int k = 0; k < a.steps; ++k) {
       const bool last = k + 1 == a.steps;
-      symsq(bp, k);  // B'
+      symsq(bp, k, dg);  // B'
       const bf16_t* xs = k == 0 ? y : uniform_ptr(reinterpret_cast<const bf16_t*>(
                                           mat_at(((k - 1) & 1) ? a.xb : a.xa, u)));
       const bf16_t* xd = last ? out : uniform_ptr(reinterpret_cast<const bf16_t*>(
                                           mat_at((k & 1) ? a.xb : a.xa, u)));
       Acc an;  // A_{k+1}
-      column_pass(xs, xd, k == 0 ? s : 1.0f, !last, an);
+      column_pass(xs, xd, k == 0 ? s : 1.0f, !last, an, dg, (k == 0 || !dg) ? nullptr : lo,
+                  (last || !dg) ? nullptr : lo);
       if (!last) store_sym(an, am, 1.0f);
     }
   } else {
@@ -344,7 +445,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     char* t = s0;
     for (int k = 0; k < a.steps; ++k) {
       char* p = k == 0 ? q : bp;
-      symsq(p, k);
+      symsq(p, k, nullptr);
       if (k > 0) {
         Acc c;
         product(p, q, c);
@@ -370,7 +471,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     }
     barrier_lds();
     Acc unused;
-    column_pass(y, out, s, false, unused);
+    column_pass(y, out, s, false, unused, nullptr, nullptr, nullptr);
   }
 }
 

@@ -78,6 +78,12 @@ bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* 
   l.scale = off; off += align_up(U * 4);
   l.zflag = off; off += align_up(U * 4);
   l.partial = off; off += align_up(U * static_cast<size_t>(l.parts) * 8);
+  if (compute == MUON_BF16) {
+    const int64_t t = l.m >= 256 ? 256 : 128;
+    l.lo_unit = static_cast<size_t>(ceil_div(l.m, t) * t) * static_cast<size_t>(ceil_div(l.n, t) * t) * 2;
+    l.lo = off; off += align_up(U * l.lo_unit);
+    l.dvec = off; off += align_up(U * static_cast<size_t>(l.m) * 4);
+  }
   l.total = count == 0 ? 0 : off;
   *L = l;
   return true;

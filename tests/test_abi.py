@@ -103,10 +103,20 @@ def test_workspace_formula(rows, cols, h, count, compute):
     parts = -(-ue // chunk)
     want = (2 * _aligned(units * m * n * e) + 2 * _aligned(units * m * m * e)
             + 2 * _aligned(units * 4) + _aligned(units * parts * 8))
+    lo = 0
+    if compute == "bf16":
+        # the iterate's residual plane, tile-padded (T = 256 once m >= 256,
+        # else 128), and B's diagonal, one float per row
+        t = 256 if m >= 256 else 128
+        lo = units * (-(-m // t) * t) * (-(-n // t) * t) * 2
+        want += _aligned(lo) + _aligned(units * m * 4)
     assert ns_workspace_bytes(rows, cols, count, h, compute) == want
-    # the stated bound: (2 + 2 m / n) x full bytes, plus small scalars
+    # the stated bound: (2 + 2 m / n) x full bytes (bf16: 3 + 2 m / n, the
+    # residual plane, up to its tile padding), plus small scalars
     full = units * m * n * e
-    assert want <= (2 + 2 * m / n) * full + 4 * 256 + units * (8 + parts * 8) + 256
+    k = 3 if compute == "bf16" else 2
+    pad = (lo - units * m * n * 2) if lo else 0
+    assert want <= (k + 2 * m / n) * full + pad + 6 * 256 + units * (12 + 4 * m + parts * 8)
 
 
 def test_workspace_rejects_bad_shapes():
@@ -134,10 +144,12 @@ def test_plan_qwen3_4b_buckets():
     assert [shapes[i][:2] for i in first.indices] == [(4096, 2560)] * 25
     assert [shapes[i][:2] for i in plan.buckets[1].indices] == [(4096, 2560)] * 11 + [(2560, 4096)] * 14
     assert plan.buckets[1].shape_groups == 2 and plan.buckets[2].shape_groups == 1
-    # workspace: stated function of the cap, (2 + 2 m/n) x full bytes at most
+    # workspace: stated function of the cap, (3 + 2 m/n) x full bytes at most
+    # in bf16 (two iterates, the iterate's residual plane, A and B'); these
+    # shapes fill whole 256-tiles, so the residual plane has no padding
     for b in plan.buckets:
-        scalars = b.units * (8 + 512 * 8) + 8 * 256 * b.shape_groups
-        assert b.workspace_bytes <= (2 + 2 * b.m / b.n) * b.full_bytes + scalars
+        scalars = b.units * (8 + 4 * b.m + 512 * 8) + 8 * 256 * b.shape_groups
+        assert b.workspace_bytes <= (3 + 2 * b.m / b.n) * b.full_bytes + scalars
     assert plan.max_workspace == max(b.workspace_bytes for b in plan.buckets)
 
 
@@ -180,8 +192,12 @@ def test_plan_workspace_cap_experts():
     assert all(b.workspace_bytes <= 1 << 30 for b in plan.buckets)
     assert all((b.m, b.n) == (768, 2048) for b in plan.buckets)
     assert sum(b.count for b in plan.buckets) == len(shapes)
-    # cross-layer merge: one canonical bucket for all expert matrices
-    assert max(b.count for b in plan.buckets) >= 100
+    # cross-layer merge: one canonical bucket for all expert matrices (gate,
+    # up and the transposed down alike), filled greedily up to the cap, so
+    # every micro-bucket but the last holds as many experts as the cap allows
+    full = [b.count for b in plan.buckets[:-1]]
+    assert full and all(c == full[0] for c in full) and plan.buckets[-1].count <= full[0]
+    assert len(plan.buckets) == -(-len(shapes) // full[0])
 
 
 def test_plan_over_cap_matrix_alone():

@@ -230,7 +230,7 @@ def test_fused_per_head_workload_sampled():
     # the per-head q/k/v of Qwen3-4B (1728 heads of 128 x 2560) take the fused
     # path by default; sampled against the oracle and against the unfused path
     w = synth.qwen3_4b_heads(layers=36)
-    c = Context(DEV, 2 << 30)
+    c = Context(DEV, 4 << 30)
     c.timing_enable(True, 64)
     g = gen(w.seed)
     mats = [synth.normal((m.rows, m.cols), w.grad_std, g, DEV, torch.bfloat16) for m in w.mats]
