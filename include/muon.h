@@ -305,6 +305,30 @@ muon_status_t muon_apply(muon_ctx_t* ctx, void* stream, float* master, const voi
                          int32_t update_dtype, void* weight_bf16, int64_t numel, float lr,
                          float scale, float weight_decay);
 
+/* Allocation-free Newton-Schulz, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, kernels and results as
+ * muon_newton_schulz_batched (bit for bit), without a context: the workspace
+ * is a static device array of MUON_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds from the first call there until the process ends
+ * (the first call on a device looks its address up; no call allocates).
+ * device: the HIP device the stream belongs to.  The call's workspace
+ * (muon_ns_workspace_bytes(shape, count, params->compute)) must fit the
+ * scratch, else MUON_EWORKSPACE.  Matrices must be evenly spaced (mats[i] =
+ * mats[0] + i * d, no overlap), and out NULL (in place), equal to mats, or
+ * evenly spaced and disjoint from every input; otherwise MUON_EINVAL.  Every
+ * call on one GPU shares that GPU's scratch: calls that overlap on one GPU
+ * (different streams or threads, without ordering) race and give undefined
+ * results.  No per-kernel timing.  muon_noalloc_last_error() gives the
+ * calling thread's last error text (a static string). */
+#define MUON_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+muon_status_t muon_newton_schulz_batched_noalloc(int device, void* stream,
+                                                 const void* const* mats, int64_t count,
+                                                 muon_shape_t shape, int32_t io_dtype,
+                                                 const muon_ns_params_t* params,
+                                                 void* const* out, int* nonfinite_flag);
+const char* muon_noalloc_last_error(void);
+
 /* ------------------------------------------------------------------------ */
 /* Diagnostics                                                               */
 /* ------------------------------------------------------------------------ */

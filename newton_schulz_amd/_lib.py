@@ -10,6 +10,7 @@ LIB_PATH = os.path.join(HERE, "libmuon.so")
 MUON_OK, MUON_EINVAL, MUON_ESHAPE, MUON_EDTYPE, MUON_EWORKSPACE, MUON_EHIP, MUON_ENOMEM = range(7)
 MUON_F32, MUON_BF16 = 0, 1
 MUON_CAP_FULL_BYTES, MUON_CAP_WORKSPACE = 0, 1
+MUON_NOALLOC_SCRATCH_BYTES = 256 << 20
 KERNEL_CLASSES = ["momentum", "norm", "gram", "symsq", "update", "apply", "prod", "fused"]
 
 # every symbol include/muon.h declares
@@ -20,6 +21,7 @@ EXPORTS = [
     "muon_plan_max_workspace", "muon_plan_destroy", "muon_momentum_update",
     "muon_newton_schulz_batched", "muon_apply", "muon_status_string", "muon_last_error",
     "muon_timing_enable", "muon_timing_reset", "muon_timing_read",
+    "muon_newton_schulz_batched_noalloc", "muon_noalloc_last_error",
 ]
 
 
@@ -80,6 +82,9 @@ def load() -> ctypes.CDLL:
         "muon_timing_enable": (i32, [vp, i32, i32]),
         "muon_timing_reset": (i32, [vp]),
         "muon_timing_read": (i32, [vp, i32, P(ctypes.c_double), P(i64)]),
+        "muon_newton_schulz_batched_noalloc": (i32, [ctypes.c_int, vp, P(vp), i64, Shape, i32,
+                                                      P(NsParams), P(vp), vp]),
+        "muon_noalloc_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -97,6 +97,37 @@ def ns_workspace_bytes(rows: int, cols: int, count: int, head_rows: int = 0,
         Shape(rows, cols, head_rows), count, MUON_BF16 if compute == "bf16" else MUON_F32))
 
 
+def newton_schulz_noalloc(mats: Sequence[torch.Tensor], out: Optional[Sequence[torch.Tensor]] = None,
+                          head_rows: int = 0, params: Optional[NsParams] = None,
+                          nonfinite_flag: Optional[torch.Tensor] = None, stream=None):
+    """muon_newton_schulz_batched_noalloc: the batched Newton-Schulz without a
+    context or any allocation (static device scratch of
+    MUON_NOALLOC_SCRATCH_BYTES per GPU).  Matrices evenly spaced; out None
+    (in place), the inputs, or disjoint from them."""
+    lib = _lib.load()
+    device = mats[0].device
+    if params is None:
+        params = ns_params(compute="bf16" if mats[0].dtype == torch.bfloat16 else "f32")
+    shape, dt = mats[0].shape, mats[0].dtype
+    for i, m in enumerate(mats):
+        _check(m, f"mats[{i}]", device)
+        if m.dim() != 2 or m.shape != shape or m.dtype != dt:
+            raise ValueError("all matrices of one call must be 2D with one shape and dtype")
+    arr_t = ctypes.c_void_p * len(mats)
+    pin = arr_t(*[m.data_ptr() for m in mats])
+    pout = None
+    if out is not None:
+        for i, o in enumerate(out):
+            _check(o, f"out[{i}]", device)
+        pout = arr_t(*[o.data_ptr() for o in out])
+    flag = ctypes.c_void_p(nonfinite_flag.data_ptr()) if nonfinite_flag is not None else None
+    st = lib.muon_newton_schulz_batched_noalloc(
+        device.index, _stream(device, stream), pin, len(mats), Shape(shape[0], shape[1], head_rows),
+        _dtype(mats[0]), ctypes.byref(params), pout, flag)
+    if st != _lib.MUON_OK:
+        raise MuonError(st, f"muon_newton_schulz_batched_noalloc: {lib.muon_noalloc_last_error().decode()}")
+
+
 class Context:
     """A libmuon context: one device and one preallocated workspace slab."""
 

@@ -364,34 +364,57 @@ void fill_table(uint64_t* dst, const void* const* p, int64_t count, int64_t per,
 
 }  // namespace
 
-extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
-                                                    const void* const* mats, int64_t count,
-                                                    muon_shape_t shape, int32_t io_dtype,
-                                                    const muon_ns_params_t* prm,
-                                                    void* const* out, int* nonfinite_flag) {
-  if (c == nullptr) return MUON_EINVAL;
-  if (count < 0) return fail(c, MUON_EINVAL, "count < 0");
-  if (prm == nullptr) return fail(c, MUON_EINVAL, "params NULL");
-  if (!is_dtype(io_dtype) || !is_dtype(prm->compute)) return fail(c, MUON_EDTYPE, "dtype");
+namespace {
+
+muon_status_t efail(const NsEnv& env, muon_status_t st, const char* what) {
+  if (env.ctx) env.ctx->err = what;
+  if (env.err) *env.err = what;
+  return st;
+}
+muon_status_t ehip(const NsEnv& env, hipError_t e, const char* where) {
+  if (env.ctx) return hip_fail(env.ctx, e, where);
+  if (env.err) *env.err = where;
+  return MUON_EHIP;
+}
+long etstart(const NsEnv& env, hipStream_t s, int cls) { return env.ctx ? tstart(env.ctx, s, cls) : -1; }
+void etstop(const NsEnv& env, hipStream_t s, long k) {
+  if (env.ctx) tstop(env.ctx, s, k);
+}
+
+}  // namespace
+
+// The Newton-Schulz driver behind both batched entry points.  env.ctx is the
+// context (workspace slab, pointer-table ring, timing events, error text), or
+// null for the allocation-free entry point, which brings its own workspace,
+// takes uniformly placed matrices only (no pointer tables) and records its
+// error text as a static string.
+muon_status_t ns_batched(const NsEnv& env, void* stream, const void* const* mats, int64_t count,
+                         muon_shape_t shape, int32_t io_dtype, const muon_ns_params_t* prm,
+                         void* const* out, int* nonfinite_flag) {
+  muon_ctx* c = env.ctx;
+
+  if (count < 0) return efail(env, MUON_EINVAL, "count < 0");
+  if (prm == nullptr) return efail(env, MUON_EINVAL, "params NULL");
+  if (!is_dtype(io_dtype) || !is_dtype(prm->compute)) return efail(env, MUON_EDTYPE, "dtype");
   if (io_dtype != prm->compute)
-    return fail(c, MUON_EDTYPE, "io dtype must equal the compute dtype");
-  if (prm->steps < 0 || !(prm->eps >= 0.0f)) return fail(c, MUON_EINVAL, "steps/eps");
+    return efail(env, MUON_EDTYPE, "io dtype must equal the compute dtype");
+  if (prm->steps < 0 || !(prm->eps >= 0.0f)) return efail(env, MUON_EINVAL, "steps/eps");
   if (prm->method != MUON_NS_QUINTIC && prm->method != MUON_NS_GRAM)
-    return fail(c, MUON_EINVAL, "method");
+    return efail(env, MUON_EINVAL, "method");
   if (prm->fuse != MUON_FUSE_AUTO && prm->fuse != MUON_FUSE_OFF && prm->fuse != MUON_FUSE_ON)
-    return fail(c, MUON_EINVAL, "fuse");
+    return efail(env, MUON_EINVAL, "fuse");
   if (prm->coeffs != nullptr)
     for (int64_t k = 0; k < 3 * static_cast<int64_t>(prm->steps); ++k)
-      if (!std::isfinite(prm->coeffs[k])) return fail(c, MUON_EINVAL, "coefficients not finite");
+      if (!std::isfinite(prm->coeffs[k])) return efail(env, MUON_EINVAL, "coefficients not finite");
   NsLayout L;
-  if (!ns_layout(shape, count, prm->compute, &L)) return fail(c, MUON_ESHAPE, "shape");
+  if (!ns_layout(shape, count, prm->compute, &L)) return efail(env, MUON_ESHAPE, "shape");
   if (count == 0) return MUON_OK;
-  if (mats == nullptr) return fail(c, MUON_EINVAL, "mats NULL");
+  if (mats == nullptr) return efail(env, MUON_EINVAL, "mats NULL");
   const size_t es = esize(io_dtype);
   for (int64_t i = 0; i < count; ++i) {
-    if (mats[i] == nullptr || (out && out[i] == nullptr)) return fail(c, MUON_EINVAL, "null matrix");
+    if (mats[i] == nullptr || (out && out[i] == nullptr)) return efail(env, MUON_EINVAL, "null matrix");
     if ((reinterpret_cast<uintptr_t>(mats[i]) % es) || (out && reinterpret_cast<uintptr_t>(out[i]) % es))
-      return fail(c, MUON_EINVAL, "misaligned matrix");
+      return efail(env, MUON_EINVAL, "misaligned matrix");
   }
   const int64_t per = L.units / count;
   const int64_t unit_elems = L.ur * L.uc;
@@ -401,23 +424,25 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   if (prm->sq_partials != nullptr) {
     if (prm->sq_base == nullptr || prm->sq_count < 0 ||
         reinterpret_cast<uintptr_t>(prm->sq_partials) % 8 || unit_elems % MUON_SQ_BLOCK)
-      return fail(c, MUON_EINVAL, "sq_partials: units must span whole blocks");
+      return efail(env, MUON_EINVAL, "sq_partials: units must span whole blocks");
     const uintptr_t base = reinterpret_cast<uintptr_t>(prm->sq_base);
     const int64_t nblk = per * (unit_elems / MUON_SQ_BLOCK);
     for (int64_t i = 0; i < count; ++i) {
       const uintptr_t a = reinterpret_cast<uintptr_t>(mats[i]);
       if (a < base || (a - base) % static_cast<uintptr_t>(block_bytes) ||
           static_cast<int64_t>((a - base) / static_cast<uintptr_t>(block_bytes)) > prm->sq_count - nblk)
-        return fail(c, MUON_EINVAL, "sq_partials do not cover a matrix on block boundaries");
+        return efail(env, MUON_EINVAL, "sq_partials do not cover a matrix on block boundaries");
     }
   }
-  if (L.total > c->ws_bytes) return fail(c, MUON_EWORKSPACE, "workspace too small for this call");
+  if (L.total > env.ws_bytes) return efail(env, MUON_EWORKSPACE, "workspace too small for this call");
   const void* const* outp = out ? reinterpret_cast<const void* const*>(out) : mats;
 
   UnitsRef in = describe(mats, count, per, unit_bytes);
   UnitsRef ot = describe(outp, count, per, unit_bytes);
+  if ((in.needs_table || ot.needs_table) && c == nullptr)
+    return efail(env, MUON_EINVAL, "matrices not evenly spaced: pointer tables need a context");
   if ((in.needs_table || ot.needs_table) && L.units > kTabCap)
-    return fail(c, MUON_EINVAL, "too many irregularly placed units in one call (max 65536)");
+    return efail(env, MUON_EINVAL, "too many irregularly placed units in one call (max 65536)");
 
   // vector paths need 16-byte aligned units
   bool al = (unit_bytes % 16) == 0;
@@ -425,7 +450,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   const bool mfma = prm->compute == MUON_BF16 && al && (L.ur % 8 == 0) && (L.uc % 8 == 0) &&
                     unit_bytes < (int64_t(1) << 31);
 
-  DeviceGuard g(c->device);
+  DeviceGuard g(env.device);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
 
@@ -434,7 +459,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     c->tab_next = (c->tab_next + 1) % kTabSlots;
     if (c->tab_used[slot]) {
       e = hipEventSynchronize(c->tab_ev[slot]);
-      if (e != hipSuccess) return hip_fail(c, e, "table slot wait");
+      if (e != hipSuccess) return ehip(env, e, "table slot wait");
     }
     uint64_t* hin = c->host_tab + static_cast<size_t>(slot) * 2 * kTabCap;
     uint64_t* hout = hin + kTabCap;
@@ -443,21 +468,21 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     if (in.needs_table) {
       fill_table(hin, mats, count, per, unit_bytes);
       e = hipMemcpyAsync(din, hin, sizeof(uint64_t) * L.units, hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) return hip_fail(c, e, "table upload");
+      if (e != hipSuccess) return ehip(env, e, "table upload");
       in.ref = MatRef{nullptr, 0, din};
     }
     if (ot.needs_table) {
       fill_table(hout, outp, count, per, unit_bytes);
       e = hipMemcpyAsync(dout, hout, sizeof(uint64_t) * L.units, hipMemcpyHostToDevice, s);
-      if (e != hipSuccess) return hip_fail(c, e, "table upload");
+      if (e != hipSuccess) return ehip(env, e, "table upload");
       ot.ref = MatRef{nullptr, 0, dout};
     }
     e = hipEventRecord(c->tab_ev[slot], s);
-    if (e != hipSuccess) return hip_fail(c, e, "table event");
+    if (e != hipSuccess) return ehip(env, e, "table event");
     c->tab_used[slot] = true;
   }
 
-  char* ws = c->ws;
+  char* ws = env.ws;
   const int64_t xbytes = L.m * L.n * static_cast<int64_t>(es);
   const int64_t abytes = L.m * L.m * static_cast<int64_t>(es);
   const MatRef XA{ws + L.xa, xbytes, nullptr}, XB{ws + L.xb, xbytes, nullptr};
@@ -477,7 +502,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     a.tiles_n = static_cast<int>((a.N + T - 1) / T);
     a.tiles_per_unit = (epi == EPI_UPDATE) ? a.tiles_m * a.tiles_n : a.tiles_m * (a.tiles_m + 1) / 2;
     a.units = L.units;
-    a.cus = c->cus;
+    a.cus = env.cus;
     a.zflag = zflag;
   };
   // (a, b, c) of iteration k: the per-iteration table's row k, else the fixed
@@ -506,22 +531,22 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   na.sq_base = static_cast<const char*>(prm->sq_base);
   na.block_bytes = block_bytes;
   na.blocks_per_unit = unit_elems / MUON_SQ_BLOCK;
-  long tk = tstart(c, s, MUON_K_NORM);
+  long tk = etstart(env, s, MUON_K_NORM);
   e = launch_norm(s, na, io_bf16, al && (unit_elems % 8 == 0));
-  tstop(c, s, tk);
-  if (e != hipSuccess) return hip_fail(c, e, "norm launch");
+  etstop(env, s, tk);
+  if (e != hipSuccess) return ehip(env, e, "norm launch");
   if (prm->steps == 0) {
     e = launch_scale_copy(s, in.ref, ot.ref, unit_elems, L.units, scale, io_bf16);
-    return e == hipSuccess ? MUON_OK : hip_fail(c, e, "copy launch");
+    return e == hipSuccess ? MUON_OK : ehip(env, e, "copy launch");
   }
   auto gemm = [&](int cls, NsGemmArgs& a, int epi, bool tm, bool tn) -> hipError_t {
     // 256 x 256 tiles once the smaller output side reaches 256
     const int T = mfma ? ((std::min(a.M, a.N) >= 256) ? 256 : 128) : 64;
     setup(a, epi, T);
-    const long k = tstart(c, s, cls);
+    const long k = etstart(env, s, cls);
     const hipError_t r = mfma ? launch_ns_gemm_mfma(s, a, epi, tm, tn, T)
                               : launch_ns_gemm_simple(s, a, epi, tm, tn, io_bf16);
-    tstop(c, s, k);
+    etstop(env, s, k);
     return r;
   };
   // Does the output touch the input?  `alias`: the spans of the inputs and
@@ -552,8 +577,9 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
   // other matrix's input.
   const bool small_ok = mfma && !tall && m <= 128 && prm->fuse != MUON_FUSE_OFF &&
                         (prm->coeffs == nullptr || prm->steps <= MUON_NS_FUSED_MAX_ROWS) &&
-                        (!alias || !cross_overlap(mats, outp, count, unit_bytes * per));
-  if (small_ok && (prm->fuse == MUON_FUSE_ON || L.units >= c->cus)) {
+                        (!alias || (c == nullptr ? env.outputs_in_place
+                                                 : !cross_overlap(mats, outp, count, unit_bytes * per)));
+  if (small_ok && (prm->fuse == MUON_FUSE_ON || L.units >= env.cus)) {
     NsSmallArgs fa{};
     fa.src = in.ref;
     fa.dst = ot.ref;
@@ -571,10 +597,10 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     fa.lo = lo_plane;
     fa.ncoef = prm->coeffs ? prm->steps : 1;
     for (int k = 0; k < fa.ncoef; ++k) coef(k, &fa.coef[k][0], &fa.coef[k][1], &fa.coef[k][2]);
-    const long k = tstart(c, s, MUON_K_FUSED);
+    const long k = etstart(env, s, MUON_K_FUSED);
     e = launch_ns_small(s, fa);
-    tstop(c, s, k);
-    return e == hipSuccess ? MUON_OK : hip_fail(c, e, "fused launch");
+    etstop(env, s, k);
+    return e == hipSuccess ? MUON_OK : ehip(env, e, "fused launch");
   }
 
   if (gram_form) {
@@ -598,7 +624,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     ga.scale = scale;
     ga.scale_pow = 2;
     e = gemm(MUON_K_GRAM, ga, EPI_GRAM, tall, tall);
-    if (e != hipSuccess) return hip_fail(c, e, "gram launch");
+    if (e != hipSuccess) return ehip(env, e, "gram launch");
     MatRef Q = R2, other = R3;
     for (int k = 0; k < prm->steps; ++k) {
       // P_k = a I + b A_k + c A_k^2; P_0 is Q_1 itself
@@ -609,17 +635,17 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
       sa.M = sa.N = sa.K = static_cast<int>(m);
       coef(k, &sa.ca, &sa.cb, &sa.cc);
       e = gemm(MUON_K_SYMSQ, sa, EPI_SYMSQ, false, false);
-      if (e != hipSuccess) return hip_fail(c, e, "symsq launch");
+      if (e != hipSuccess) return ehip(env, e, "symsq launch");
       if (k > 0) {
         e = sym_prod(MUON_K_PROD, P, Q, other);  // Q_{k+1} = P_k Q_k
-        if (e != hipSuccess) return hip_fail(c, e, "product launch");
+        if (e != hipSuccess) return ehip(env, e, "product launch");
         std::swap(Q, other);
       }
       if (k + 1 < prm->steps) {
         // A_{k+1} = (P_k A_k) P_k, through the free region
         e = sym_prod(MUON_K_PROD, P, AR, other);
         if (e == hipSuccess) e = sym_prod(MUON_K_PROD, other, P, AR);
-        if (e != hipSuccess) return hip_fail(c, e, "product launch");
+        if (e != hipSuccess) return ehip(env, e, "product launch");
       }
     }
     // X = s Q X_0 (tall: Y Q).  Written straight to the output unless the
@@ -645,10 +671,10 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     }
     ua.K = static_cast<int>(m);
     e = gemm(MUON_K_UPDATE, ua, EPI_UPDATE, false, !tall);
-    if (e != hipSuccess) return hip_fail(c, e, "update launch");
+    if (e != hipSuccess) return ehip(env, e, "update launch");
     if (alias) {
       e = launch_scale_copy(s, freeX, ot.ref, unit_elems, L.units, nullptr, io_bf16);
-      if (e != hipSuccess) return hip_fail(c, e, "copy launch");
+      if (e != hipSuccess) return ehip(env, e, "copy launch");
     }
     return MUON_OK;
   }
@@ -668,7 +694,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     ga.scale = scale;
     ga.scale_pow = (k == 0) ? 2 : 0;
     e = gemm(MUON_K_GRAM, ga, EPI_GRAM, tall, tall);
-    if (e != hipSuccess) return hip_fail(c, e, "gram launch");
+    if (e != hipSuccess) return ehip(env, e, "gram launch");
 
     NsGemmArgs sa{};
     sa.pm = AR; sa.pn = AR; sa.dst = BR; sa.epi = AR;
@@ -677,7 +703,7 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     sa.dvec = dvec;
     coef(k, &sa.ca, &sa.cb, &sa.cc);
     e = gemm(MUON_K_SYMSQ, sa, EPI_SYMSQ, false, false);
-    if (e != hipSuccess) return hip_fail(c, e, "symsq launch");
+    if (e != hipSuccess) return ehip(env, e, "symsq launch");
 
     NsGemmArgs ua{};
     ua.dst = dstX;
@@ -709,11 +735,26 @@ extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
     }
     ua.K = static_cast<int>(m);
     e = gemm(MUON_K_UPDATE, ua, EPI_UPDATE, false, !tall);
-    if (e != hipSuccess) return hip_fail(c, e, "update launch");
+    if (e != hipSuccess) return ehip(env, e, "update launch");
   }
   if (prm->steps == 1) {
     e = launch_scale_copy(s, XA, ot.ref, unit_elems, L.units, nullptr, io_bf16);
-    if (e != hipSuccess) return hip_fail(c, e, "copy launch");
+    if (e != hipSuccess) return ehip(env, e, "copy launch");
   }
   return MUON_OK;
+}
+
+extern "C" muon_status_t muon_newton_schulz_batched(muon_ctx_t* c, void* stream,
+                                                    const void* const* mats, int64_t count,
+                                                    muon_shape_t shape, int32_t io_dtype,
+                                                    const muon_ns_params_t* prm,
+                                                    void* const* out, int* nonfinite_flag) {
+  if (c == nullptr) return MUON_EINVAL;
+  NsEnv env;
+  env.ctx = c;
+  env.ws = c->ws;
+  env.ws_bytes = c->ws_bytes;
+  env.cus = c->cus;
+  env.device = c->device;
+  return ns_batched(env, stream, mats, count, shape, io_dtype, prm, out, nonfinite_flag);
 }

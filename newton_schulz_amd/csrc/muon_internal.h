@@ -111,3 +111,21 @@ __host__ __device__ __forceinline__ void upper_tile(int t, int& ti, int& tj) {
   tj = j;
   ti = t - j * (j + 1) / 2;
 }
+
+// Where one batched Newton-Schulz call runs: a context's slab, or (ctx null)
+// the allocation-free entry point's static scratch.  outputs_in_place (ctx
+// null only): every output is its own input or all outputs are disjoint from
+// every input, as that entry point checks before the call.
+struct muon_ctx;
+struct NsEnv {
+  muon_ctx* ctx = nullptr;
+  char* ws = nullptr;
+  size_t ws_bytes = 0;
+  int cus = 256;
+  int device = 0;
+  bool outputs_in_place = false;
+  const char** err = nullptr;  // receives a static error text (ctx null)
+};
+muon_status_t ns_batched(const NsEnv& env, void* stream, const void* const* mats, int64_t count,
+                         muon_shape_t shape, int32_t io_dtype, const muon_ns_params_t* prm,
+                         void* const* out, int* nonfinite_flag);
