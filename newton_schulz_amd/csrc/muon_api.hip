@@ -711,13 +711,16 @@ muon_status_t ns_batched(const NsEnv& env, void* stream, const void* const* mats
     ua.scale_pow = (k == 0) ? 1 : 0;
     ua.zero_write = last ? 1 : 0;
     // B's diagonal completed in fp32 and the residual carried from update to
-    // update (read and rewritten tile by tile, in place); the generic kernel
-    // reads the iterate at the output position through epi
+    // update (read and rewritten tile by tile, in place) out of every update
+    // but the last two: rounding left in the second-to-last update is lifted
+    // by one more iteration only (a bf16 emulation of rank-deficient inputs
+    // moves by at most 1e-3 relative).  The generic kernel reads the iterate
+    // at the output position through epi.
     ua.dvec = dvec;
     ua.epi = src;
     ua.lde = tall ? m : n;
-    ua.lo_in = (k == 0 || lo_plane == nullptr) ? nullptr : lo_plane;
-    ua.lo_out = last ? nullptr : lo_plane;
+    ua.lo_in = (lo_plane != nullptr && ns_lo_read(k, prm->steps)) ? lo_plane : nullptr;
+    ua.lo_out = (lo_plane != nullptr && ns_lo_written(k, prm->steps)) ? lo_plane : nullptr;
     if (!tall) {
       // X' = B' X : rows from B', columns from X (K-major)
       ua.pm = BR; ua.ldm = m;

@@ -129,3 +129,8 @@ struct NsEnv {
 muon_status_t ns_batched(const NsEnv& env, void* stream, const void* const* mats, int64_t count,
                          muon_shape_t shape, int32_t io_dtype, const muon_ns_params_t* prm,
                          void* const* out, int* nonfinite_flag);
+
+// Which updates of a `steps`-iteration call keep the iterate's residual: it
+// is written by updates 0 .. steps - 3 and read by the update after each.
+__host__ __device__ __forceinline__ bool ns_lo_written(int k, int steps) { return k + 3 <= steps; }
+__host__ __device__ __forceinline__ bool ns_lo_read(int k, int steps) { return k >= 1 && k + 2 <= steps; }

@@ -433,8 +433,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       const bf16_t* xd = last ? out : uniform_ptr(reinterpret_cast<const bf16_t*>(
                                           mat_at((k & 1) ? a.xb : a.xa, u)));
       Acc an;  // A_{k+1}
-      column_pass(xs, xd, k == 0 ? s : 1.0f, !last, an, dg, (k == 0 || !dg) ? nullptr : lo,
-                  (last || !dg) ? nullptr : lo);
+      column_pass(xs, xd, k == 0 ? s : 1.0f, !last, an, dg,
+                  (dg && ns_lo_read(k, a.steps)) ? lo : nullptr,
+                  (dg && ns_lo_written(k, a.steps)) ? lo : nullptr);
       if (!last) store_sym(an, am, 1.0f);
     }
   } else {
