@@ -56,6 +56,14 @@ __device__ __forceinline__ void dma16(const __amdgpu_buffer_rsrc_t& r, char* lds
 // before each barrier), and no conservative wait for the most recent load is
 // inserted ahead of LDS reads of other stage buffers.  M0 holds the LDS
 // destination of the wave's 1 KiB block.
+//
+// The compiler does not look inside inline asm for hazards, so the asm keeps
+// its own: a vector-ALU write of an SGPR (v_readlane reloading a spilled
+// scalar, v_readfirstlane) needs 5 wait states before a vector-memory
+// instruction reads that SGPR (descriptor, offset), and an M0 write needs 1
+// before an LDS-DMA load.  Without them the load may take a stale offset and
+// fill the stage with the wrong data, depending on where register pressure
+// places the reloads.
 __device__ __forceinline__ u32x4_t rsrc_words(const void* p, uint32_t bytes) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);
   return u32x4_t{static_cast<uint32_t>(v), static_cast<uint32_t>(v >> 32) & 0xffffu, bytes,
@@ -64,9 +72,53 @@ __device__ __forceinline__ u32x4_t rsrc_words(const void* p, uint32_t bytes) {
 __device__ __forceinline__ void dma16_asm(const u32x4_t& r, char* lds, uint32_t voff,
                                           uint32_t soff) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds));
-  asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff),
-               "{m0}"(m0)
-               : "memory");
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff),
+      "s"(r), "s"(soff), "s"(m0)
+      : "memory", "m0");
+}
+// Four such loads from one descriptor and offset in one asm block, so the
+// five wait states are paid once for the four.
+__device__ __forceinline__ void dma16x4_asm(const u32x4_t& r, char* const (&lds)[4],
+                                            const uint32_t (&voff)[4], uint32_t soff) {
+  const uint32_t m0[4] = {static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds[0])),
+                          static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds[1])),
+                          static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds[2])),
+                          static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)lds[3]))};
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b32 m0, %6\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %4, %5 offen lds\n\t"
+      "s_mov_b32 m0, %7\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %1, %4, %5 offen lds\n\t"
+      "s_mov_b32 m0, %8\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %4, %5 offen lds\n\t"
+      "s_mov_b32 m0, %9\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %3, %4, %5 offen lds" ::"v"(voff[0]),
+      "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(r), "s"(soff), "s"(m0[0]), "s"(m0[1]),
+      "s"(m0[2]), "s"(m0[3])
+      : "memory", "m0");
+}
+// NG loads of one operand stage: groups of four, then singles.
+template <int NG, typename FL, typename FV>
+__device__ __forceinline__ void dma16_group(const u32x4_t& r, uint32_t soff, FL&& lds_of, FV&& voff_of) {
+  static_assert(NG >= 1, "no loads");
+  constexpr int G4 = NG / 4;
+#pragma unroll
+  for (int g = 0; g < G4; ++g) {
+    char* const l[4] = {lds_of(4 * g), lds_of(4 * g + 1), lds_of(4 * g + 2), lds_of(4 * g + 3)};
+    const uint32_t v[4] = {voff_of(4 * g), voff_of(4 * g + 1), voff_of(4 * g + 2), voff_of(4 * g + 3)};
+    dma16x4_asm(r, l, v, soff);
+  }
+#pragma unroll
+  for (int q = 4 * G4; q < NG; ++q) dma16_asm(r, lds_of(q), voff_of(q), soff);
 }
 
 // Four consecutive k of one column of a row-major [k][col] LDS tile per lane

@@ -164,10 +164,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       base[q] = row < m ? static_cast<uint32_t>((static_cast<int64_t>(row) * n + 8 * lc) * 2) : kOOB;
     }
     auto issue = [&](char* st, int k0) {
-#pragma unroll
-      for (int q = 0; q < NGR; ++q)
-        dma16_asm(rs, st + (wave + NWV * q) * 1024, k0 + kc[q] < n ? base[q] : kOOB,
-                  static_cast<uint32_t>(k0 * 2));
+      dma16_group<NGR>(
+          rs, static_cast<uint32_t>(k0 * 2), [&](int q) { return st + (wave + NWV * q) * 1024; },
+          [&](int q) { return k0 + kc[q] < n ? base[q] : kOOB; });
     };
     Acc acc;
     acc.zero();
@@ -291,10 +290,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       base[q] = kr < m ? static_cast<uint32_t>((static_cast<int64_t>(kr) * n + col) * 2) : kOOB;
     }
     auto issue = [&](char* sl, int c0) {
-#pragma unroll
-      for (int q = 0; q < NGC; ++q)
-        dma16_asm(rs, sl + (wave + NWV * q) * 1024, c0 + cc[q] < n ? base[q] : kOOB,
-                  static_cast<uint32_t>(c0 * 2));
+      dma16_group<NGC>(
+          rs, static_cast<uint32_t>(c0 * 2), [&](int q) { return sl + (wave + NWV * q) * 1024; },
+          [&](int q) { return c0 + cc[q] < n ? base[q] : kOOB; });
     };
     an.zero();
     issue(s0, 0);
