@@ -76,9 +76,9 @@ struct Operand<R, false, NW, BK> {
   __device__ __forceinline__ void issue(char* lds, int k0, int K, int64_t /*ld*/, int wave,
                                         bool full) const {
     const uint32_t soff = static_cast<uint32_t>(k0 * 2);
-#pragma unroll
-    for (int q = 0; q < NG; ++q)
-      dma16_asm(rsrc, lds + (wave + NW * q) * 1024, (full || k0 + kc[q] < K) ? base[q] : kOOB, soff);
+    dma16_group<NG>(
+        rsrc, soff, [&](int q) { return lds + (wave + NW * q) * 1024; },
+        [&](int q) { return (full || k0 + kc[q] < K) ? base[q] : kOOB; });
   }
   // MFMA operand for tile rows rb .. rb + 31, k = 16 kk + 8 (lane / 32) + 0..7
   __device__ __forceinline__ bf16x8_t frag(const char* t, int rb, int kk, int lane) const {
@@ -112,9 +112,9 @@ struct Operand<R, true, NW, BK> {
   __device__ __forceinline__ void issue(char* lds, int k0, int K, int64_t ld, int wave,
                                         bool full) const {
     const uint32_t soff = static_cast<uint32_t>(static_cast<int64_t>(k0) * ld * 2);
-#pragma unroll
-    for (int q = 0; q < NG; ++q)
-      dma16_asm(rsrc, lds + (wave + NW * q) * 1024, (full || k0 + kr[q] < K) ? base[q] : kOOB, soff);
+    dma16_group<NG>(
+        rsrc, soff, [&](int q) { return lds + (wave + NW * q) * 1024; },
+        [&](int q) { return (full || k0 + kr[q] < K) ? base[q] : kOOB; });
   }
   __device__ __forceinline__ bf16x8_t frag(const char* t, int rb, int kk, int lane) const {
     const int gq = lane >> 4, j = lane & 15;
@@ -208,23 +208,43 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   const int64_t t_end = rr ? total : total * (P + cnt) / G;
   const int64_t t_step = rr ? G : cnt;
 
+  // unit and tile coordinates of logical tile l
+  auto coords = [&](int64_t l, int64_t& uu, int& ti, int& tj) __attribute__((always_inline)) {
+    uu = l / a.tiles_per_unit;
+    const int t = static_cast<int>(l - uu * a.tiles_per_unit);
+    if (EPI == EPI_UPDATE) {
+      // grouped raster: bands of up to GN tile columns, row-major inside a
+      // band, so the ~32 tiles an XCD runs at once form an 8 x 4 block that
+      // shares its operand panels in L2
+      constexpr int GN = 4;
+      const int band = t / (a.tiles_m * GN);
+      const int w = min(GN, a.tiles_n - band * GN);
+      const int r = t - band * a.tiles_m * GN;
+      ti = r / w;
+      tj = band * GN + r % w;
+    } else {
+      upper_tile(t, ti, tj);
+    }
+  };
+  // corrected update: B's fp32 diagonal along the tile's diagonal side
+  // (rows for X' = B'X, columns for Y' = YB'); thread i < DS holds entry i.
+  // The next tile's entry is requested during this tile, so the load's
+  // latency is hidden.
+  const bool upd_corr = EPI == EPI_UPDATE && a.dvec != nullptr;
+  auto load_d = [&](int64_t l) __attribute__((always_inline)) {
+    int64_t uu;
+    int ti, tj;
+    coords(l, uu, ti, tj);
+    const int d0 = TN ? ti * BM : tj * BN, dlim = TN ? a.M : a.N;
+    return (tid < DS && d0 + tid < dlim) ? a.dvec[uu * static_cast<int64_t>(a.K) + d0 + tid] : 0.0f;
+  };
+  float dpre = 0.0f;
+  int64_t dpre_lid = -1;
+
   for (int64_t lid = t_first; lid < t_end; lid += t_step) {
-  const int64_t u = lid / a.tiles_per_unit;
-  const int t = static_cast<int>(lid - u * a.tiles_per_unit);
+  int64_t u;
   int ti, tj;
-  if (EPI == EPI_UPDATE) {
-    // grouped raster: bands of up to GN tile columns, row-major inside a
-    // band, so the ~32 tiles an XCD runs at once form an 8 x 4 block that
-    // shares its operand panels in L2
-    constexpr int GN = 4;
-    const int band = t / (a.tiles_m * GN);
-    const int w = min(GN, a.tiles_n - band * GN);
-    const int r = t - band * a.tiles_m * GN;
-    ti = r / w;
-    tj = band * GN + r % w;
-  } else {
-    upper_tile(t, ti, tj);
-  }
+  coords(lid, u, ti, tj);
   const int m0 = ti * BM, n0 = tj * BN;
 
   const bool zero_unit = a.zflag != nullptr && a.zflag[u] != 0;
@@ -240,17 +260,19 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   // diagonal along the output's rows (wide, X' = B'X) or columns (tall,
   // Y' = YB').  Not for a zero unit: it writes zeros and its workspace was
   // never filled.
-  const bool corr = EPI == EPI_UPDATE && a.dvec != nullptr && !zero_unit;
-  const int64_t dbase = u * static_cast<int64_t>(a.K);
+  const bool corr = upd_corr && !zero_unit;
   if (corr) {
-    const int d0 = TN ? m0 : n0, dlim = TN ? a.M : a.N;
-    for (int i = tid; i < DS; i += NT) {
-      const float d = d0 + i < dlim ? a.dvec[dbase + d0 + i] : 0.0f;
-      corr_d[i] = d;
-      corr_r[i] = muon::f32_to_bf16(muon::ns_diag_residual(d));
+    const float d = dpre_lid == lid ? dpre : load_d(lid);
+    if (tid < DS) {
+      corr_d[tid] = d;
+      corr_r[tid] = muon::f32_to_bf16(muon::ns_diag_residual(d));
     }
     // visible to every wave at the k-loop's first barrier
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  }
+  if (upd_corr && lid + t_step < t_end) {
+    dpre = load_d(lid + t_step);
+    dpre_lid = lid + t_step;
   }
 
   if (!zero_unit) {
@@ -315,22 +337,22 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
     // more MFMA per accumulator of that 32-block: acc += r hi, exactly, with
     // no vector-ALU write to the accumulators inside the loop.  A lane's
     // slice row holds at most one nonzero k.
-    auto diag_frag = [&](int idx, int k16) __attribute__((always_inline)) {
+    auto diag_frag = [&](int idx, int k16, uint32_t rv) __attribute__((always_inline)) {
       const int e = idx - k16 - 8 * (lane >> 5);  // which of the lane's 8 k is idx
-      const uint32_t rb = (e >= 0 && e < 8) ? static_cast<uint32_t>(corr_r[idx]) : 0u;
+      const uint32_t rb = (e >= 0 && e < 8) ? rv : 0u;
       const uint32_t w = (e & 1) ? (rb << 16) : rb;
       const int q = e >> 1;
       const u32x4_t v = {q == 0 ? w : 0u, q == 1 ? w : 0u, q == 2 ? w : 0u, q == 3 ? w : 0u};
       return __builtin_bit_cast(bf16x8_t, v);
     };
-    auto diag_mfmas = [&](int kt, auto KI, auto BUF) __attribute__((always_inline)) {
+    auto diag_mfmas = [&](int kt, auto KI, auto BUF, const uint32_t (&rv)[2]) __attribute__((always_inline)) {
       constexpr int kk = decltype(KI)::value, b = decltype(BUF)::value;
       const int k16 = kt * BK + 16 * kk - (TN ? m0 : n0);
       if constexpr (TN) {
         // rows k16 .. k16 + 15: wave row wm = k16 / WM, block (k16 % WM) / 32
         if (corr && k16 >= 0 && k16 < BM && k16 / WM == wm) {
           const int mis = (k16 % WM) / 32;
-          const bf16x8_t fd = diag_frag(wm * WM + mis * 32 + (lane & 31), k16);
+          const bf16x8_t fd = diag_frag(wm * WM + mis * 32 + (lane & 31), k16, rv[kk / 2]);
           static_for<FM>([&](auto MI) __attribute__((always_inline)) {
             constexpr int mi = decltype(MI)::value;
             if (mi == mis) {
@@ -345,7 +367,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
         // columns k16 .. k16 + 15: wave column wn = k16 / WN, block (k16 % WN) / 32
         if (corr && k16 >= 0 && k16 < BN && k16 / WN == wn) {
           const int nis = (k16 % WN) / 32;
-          const bf16x8_t fd = diag_frag(wn * WN + nis * 32 + (lane & 31), k16);
+          const bf16x8_t fd = diag_frag(wn * WN + nis * 32 + (lane & 31), k16, rv[kk / 2]);
           static_for<FN>([&](auto NI) __attribute__((always_inline)) {
             constexpr int ni = decltype(NI)::value;
             if (ni == nis) {
@@ -363,6 +385,16 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
       char* cur = buf(S);
       const char* nxt = buf(ic<decltype(S)::value + 1>{});
       const int kt_cur = kt_new - NS;
+      // the stage's diagonal residuals, read once: entries r0 + l % 32 and
+      // r0 + 32 + l % 32 of this tile's diagonal side (none outside it)
+      uint32_t rv[2] = {0u, 0u};
+      if constexpr (EPI == EPI_UPDATE) {
+        const int r0 = kt_cur * BK - (TN ? m0 : n0);
+        if (corr && r0 >= 0 && r0 < (TN ? BM : BN)) {
+          rv[0] = corr_r[r0 + (lane & 31)];
+          rv[1] = corr_r[r0 + 32 + (lane & 31)];
+        }
+      }
       static_for<KK>([&](auto KI) {
         constexpr int kk = decltype(KI)::value;
         constexpr int b = kk & 1;
@@ -371,7 +403,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
           mfmas(ic<b>{}, ic<0>{}, ic<NMF>{});
           interleave(ic<NMF>{});
           __builtin_amdgcn_sched_barrier(0);
-          if constexpr (EPI == EPI_UPDATE) diag_mfmas(kt_cur, ic<kk>{}, ic<b>{});
+          if constexpr (EPI == EPI_UPDATE) diag_mfmas(kt_cur, ic<kk>{}, ic<b>{}, rv);
         } else {
           mfmas(ic<b>{}, ic<0>{}, ic<NMF - TAIL>{});
           __builtin_amdgcn_sched_barrier(0);
@@ -384,7 +416,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
           mfmas(ic<b>{}, ic<NMF - TAIL>{}, ic<NMF>{});
           interleave(ic<TAIL>{});
           __builtin_amdgcn_sched_barrier(0);
-          if constexpr (EPI == EPI_UPDATE) diag_mfmas(kt_cur, ic<kk>{}, ic<b>{});
+          if constexpr (EPI == EPI_UPDATE) diag_mfmas(kt_cur, ic<kk>{}, ic<b>{}, rv);
         }
       });
     };
@@ -502,7 +534,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
           const float f = zero_unit ? 0.0f : s;  // a zero unit's update writes zeros
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = f * v[q];
-          if (corr) {
+          if (corr && a.lo_out) {
             float r[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) r[q] = v[q] - muon::bf16_round(v[q]);
