@@ -132,7 +132,7 @@ typedef struct {
 } muon_shape_t;
 
 typedef struct muon_ctx muon_ctx_t;
-typedef struct muon_plan muon_plan_t;
+typedef struct muon_plan_s muon_plan_t;
 
 /* ------------------------------------------------------------------------ */
 /* Context and workspace                                                     */
@@ -178,13 +178,25 @@ muon_status_t muon_ns_minimax_coeffs(int32_t steps, double lo, double margin, fl
                                      double* bound);
 
 /* Workspace one muon_newton_schulz_batched call needs for `count` matrices
- * of `shape` in compute dtype `compute` (pure host function).  Per Newton-
- * Schulz unit of m x n (m = min, n = max of its rows and cols, e = element
- * bytes of the compute dtype): two iterate buffers (2 e m n) + A and B
- * (2 e m^2) + 8 bytes of scalars + 8 bytes per norm partial (at most 512),
- * each region rounded up to 256 bytes: (2 + 2 m/n) x the unit's e m n bytes
- * plus scalars.  Returns 0 for an invalid shape. */
+ * of `shape` in compute dtype `compute` (pure host function; blog section
+ * "Memory control", item 2).  Per Newton-Schulz unit of m x n (m = min, n =
+ * max of its rows and cols, e = element bytes of the compute dtype): two
+ * iterate buffers (2 e m n) + A and B (2 e m^2) + 8 bytes of scalars + 8
+ * bytes per norm partial (at most 512); in BF16 also the iterate's rounding
+ * residual (2 bytes per element, rows and columns padded to the tile: 256
+ * once m >= 256, else 128) and B's diagonal in fp32 (4 m).  Each region is
+ * rounded up to 256 bytes: (2 + 2 m/n) x the unit's e m n bytes (BF16:
+ * 3 + 2 m/n, up to the residual's padding) plus scalars.  Returns 0 for an
+ * invalid shape or count <= 0. */
 size_t muon_ns_workspace_bytes(muon_shape_t shape, int64_t count, int32_t compute);
+
+/* Workspace to run Newton-Schulz over a list of matrices of mixed shapes,
+ * one muon_newton_schulz_batched call per group of identical shapes
+ * (rows, cols, head_rows), the calls one after another on one context: the
+ * largest group's muon_ns_workspace_bytes (blog section "Memory control",
+ * item 2: the workspace is a stated function of what one call holds).  Pure
+ * host function.  Returns 0 when count <= 0 or a shape is invalid. */
+size_t muon_workspace_bytes(const muon_shape_t* shapes, int64_t count, int32_t compute);
 
 /* ------------------------------------------------------------------------ */
 /* Host scheduler: same-shape buckets split into micro-buckets under a cap   */
@@ -204,6 +216,7 @@ typedef struct {
   size_t workspace_bytes;     /* sum of muon_ns_workspace_bytes per shape group */
   int32_t over_cap;           /* 1 if a single matrix alone exceeds the cap     */
   int32_t shape_groups;       /* distinct (rows, cols, head_rows) runs inside   */
+  int64_t elem_offset;        /* its first element in the plan's flat layout   */
 } muon_bucket_info_t;
 
 /* Group `count` matrices into buckets by canonical unit shape (m, n) in order
@@ -224,14 +237,32 @@ typedef struct {
 muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t count, size_t cap_bytes,
                                int32_t cap_kind, int32_t compute, int32_t compute_units,
                                muon_plan_t** out);
+/* muon_plan_create with BF16 compute and the plain cap-filling cuts
+ * (compute_units = 0): the scheduler's signature with the cap and its kind
+ * only (blog sections "Chunked communication" and "Memory control", items 1
+ * and 6). */
+muon_status_t muon_plan(const muon_shape_t* shapes, int64_t count, size_t cap_bytes,
+                        int32_t cap_kind, muon_plan_t** out);
+/* Number of micro-buckets (blog section "Chunked communication"). */
 int64_t muon_plan_num_buckets(const muon_plan_t* plan);
-/* Info on micro-bucket `b`; when `indices` is non-NULL it receives info->count
- * matrix indices (positions in the `shapes` array), in execution order. */
+/* Info on micro-bucket `b`.  When non-NULL, `indices` receives info->count
+ * matrix indices (positions in the `shapes` array) in execution order, and
+ * `offsets` the element offset of each of those matrices in the plan's flat
+ * layout: state buffers (gradients, momentum, weights) that hold every matrix
+ * in plan order -- micro-bucket after micro-bucket, members packed in
+ * execution order -- so that each micro-bucket is one contiguous range
+ * starting at info->elem_offset (blog section "DBuffer": addresses planned
+ * once at init, views per step).  Errors: MUON_EINVAL (NULL plan or info, b
+ * out of range). */
 muon_status_t muon_plan_bucket(const muon_plan_t* plan, int64_t b, muon_bucket_info_t* info,
-                               int64_t* indices);
+                               int64_t* indices, int64_t* offsets);
+/* Elements of the plan's flat layout (the sum of every matrix's rows x cols). */
+int64_t muon_plan_total_elems(const muon_plan_t* plan);
 /* Largest workspace_bytes over the plan's micro-buckets: a context this large
- * runs every micro-bucket. */
+ * runs every micro-bucket (blog section "Memory control", item 2: one
+ * preallocated workspace sized by the cap). */
 size_t muon_plan_max_workspace(const muon_plan_t* plan);
+/* Free a plan (NULL is accepted). */
 void muon_plan_destroy(muon_plan_t* plan);
 
 /* ------------------------------------------------------------------------ */

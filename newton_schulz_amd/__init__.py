@@ -6,6 +6,7 @@ library is loaded on first use and its absence raises an error.
 """
 from .api import (  # noqa: F401
     Context, MuonError, Plan, minimax_coeffs, newton_schulz_noalloc, ns_params, ns_workspace_bytes,
+    workspace_bytes,
 )
 from .muon_step import MuonStep  # noqa: F401
 from . import _lib  # noqa: F401

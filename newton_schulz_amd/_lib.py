@@ -22,6 +22,7 @@ EXPORTS = [
     "muon_newton_schulz_batched", "muon_apply", "muon_status_string", "muon_last_error",
     "muon_timing_enable", "muon_timing_reset", "muon_timing_read",
     "muon_newton_schulz_batched_noalloc", "muon_noalloc_last_error",
+    "muon_plan", "muon_plan_total_elems", "muon_workspace_bytes",
 ]
 
 
@@ -42,7 +43,8 @@ class BucketInfo(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int64), ("n", ctypes.c_int64), ("count", ctypes.c_int64),
                 ("units", ctypes.c_int64), ("numel", ctypes.c_int64),
                 ("full_bytes", ctypes.c_size_t), ("workspace_bytes", ctypes.c_size_t),
-                ("over_cap", ctypes.c_int32), ("shape_groups", ctypes.c_int32)]
+                ("over_cap", ctypes.c_int32), ("shape_groups", ctypes.c_int32),
+                ("elem_offset", ctypes.c_int64)]
 
 
 _LIB = None
@@ -70,7 +72,10 @@ def load() -> ctypes.CDLL:
         "muon_ns_workspace_bytes": (sz, [Shape, i64, i32]),
         "muon_plan_create": (i32, [P(Shape), i64, sz, i32, i32, i32, P(vp)]),
         "muon_plan_num_buckets": (i64, [vp]),
-        "muon_plan_bucket": (i32, [vp, i64, P(BucketInfo), P(i64)]),
+        "muon_plan": (i32, [P(Shape), i64, sz, i32, P(vp)]),
+        "muon_plan_bucket": (i32, [vp, i64, P(BucketInfo), P(i64), P(i64)]),
+        "muon_plan_total_elems": (i64, [vp]),
+        "muon_workspace_bytes": (sz, [P(Shape), i64, i32]),
         "muon_plan_max_workspace": (sz, [vp]),
         "muon_plan_destroy": (None, [vp]),
         "muon_momentum_update": (i32, [vp, vp, vp, i32, vp, vp, i32, i64, f32, i32]),

@@ -97,6 +97,14 @@ def ns_workspace_bytes(rows: int, cols: int, count: int, head_rows: int = 0,
         Shape(rows, cols, head_rows), count, MUON_BF16 if compute == "bf16" else MUON_F32))
 
 
+def workspace_bytes(shapes: Sequence[Tuple[int, int, int]], compute: str = "bf16") -> int:
+    """muon_workspace_bytes: workspace for Newton-Schulz over mixed shapes, one
+    call per shape group, one after another on one context."""
+    arr = (Shape * max(len(shapes), 1))(*[Shape(r, c, h) for (r, c, h) in shapes])
+    return int(_lib.load().muon_workspace_bytes(arr, len(shapes),
+                                                MUON_BF16 if compute == "bf16" else MUON_F32))
+
+
 def newton_schulz_noalloc(mats: Sequence[torch.Tensor], out: Optional[Sequence[torch.Tensor]] = None,
                           head_rows: int = 0, params: Optional[NsParams] = None,
                           nonfinite_flag: Optional[torch.Tensor] = None, stream=None):
@@ -285,6 +293,8 @@ class BucketInfo:
     over_cap: bool
     shape_groups: int
     indices: List[int]
+    elem_offset: int = 0
+    offsets: List[int] = None
 
 
 class Plan:
@@ -305,12 +315,15 @@ class Plan:
             self.buckets: List[BucketInfo] = []
             for b in range(lib.muon_plan_num_buckets(h)):
                 info = _lib.BucketInfo()
-                lib.muon_plan_bucket(h, b, ctypes.byref(info), None)
+                lib.muon_plan_bucket(h, b, ctypes.byref(info), None, None)
                 idx = (ctypes.c_int64 * info.count)()
-                lib.muon_plan_bucket(h, b, ctypes.byref(info), idx)
+                off = (ctypes.c_int64 * info.count)()
+                lib.muon_plan_bucket(h, b, ctypes.byref(info), idx, off)
                 self.buckets.append(BucketInfo(info.m, info.n, info.count, info.units, info.numel,
                                                info.full_bytes, info.workspace_bytes,
-                                               bool(info.over_cap), info.shape_groups, list(idx)))
+                                               bool(info.over_cap), info.shape_groups, list(idx),
+                                               info.elem_offset, list(off)))
             self.max_workspace = int(lib.muon_plan_max_workspace(h))
+            self.total_elems = int(lib.muon_plan_total_elems(h))
         finally:
             lib.muon_plan_destroy(h)

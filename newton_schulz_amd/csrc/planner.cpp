@@ -98,11 +98,13 @@ extern "C" size_t muon_ns_workspace_bytes(muon_shape_t shape, int64_t count, int
 struct MicroBucket {
   muon_bucket_info_t info;
   std::vector<int64_t> idx;
+  std::vector<int64_t> off;  // element offset of each member in the flat layout
 };
 
-struct muon_plan {
+struct muon_plan_s {
   std::vector<MicroBucket> buckets;
   size_t max_ws = 0;
+  int64_t total = 0;  // elements of the flat layout
 };
 
 static bool same_shape(const muon_shape_t& x, const muon_shape_t& y) {
@@ -121,7 +123,7 @@ extern "C" muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t co
     NsLayout l;
     if (!ns_layout(shapes[i], 1, compute, &l)) return MUON_ESHAPE;
   }
-  muon_plan* plan = new (std::nothrow) muon_plan;
+  muon_plan_t* plan = new (std::nothrow) muon_plan_t;
   if (plan == nullptr) return MUON_ENOMEM;
   try {
     // buckets by canonical unit shape, in order of first appearance
@@ -188,6 +190,13 @@ extern "C" muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t co
           r = q;
         }
         in.full_bytes = e * static_cast<size_t>(in.numel);
+        // flat layout: micro-buckets one after another, members packed in
+        // execution order
+        in.elem_offset = plan->total;
+        for (int64_t i : cur) {
+          mb.off.push_back(plan->total);
+          plan->total += shapes[i].rows * shapes[i].cols;
+        }
         plan->max_ws = std::max(plan->max_ws, in.workspace_bytes);
         plan->buckets.push_back(std::move(mb));
         cur.clear();
@@ -258,15 +267,46 @@ extern "C" int64_t muon_plan_num_buckets(const muon_plan_t* plan) {
   return plan ? static_cast<int64_t>(plan->buckets.size()) : 0;
 }
 
+extern "C" muon_status_t muon_plan(const muon_shape_t* shapes, int64_t count, size_t cap_bytes,
+                                   int32_t cap_kind, muon_plan_t** out) {
+  return muon_plan_create(shapes, count, cap_bytes, cap_kind, MUON_BF16, 0, out);
+}
+
 extern "C" muon_status_t muon_plan_bucket(const muon_plan_t* plan, int64_t b,
-                                          muon_bucket_info_t* info, int64_t* indices) {
+                                          muon_bucket_info_t* info, int64_t* indices,
+                                          int64_t* offsets) {
   if (plan == nullptr || info == nullptr) return MUON_EINVAL;
   if (b < 0 || b >= static_cast<int64_t>(plan->buckets.size())) return MUON_EINVAL;
   const MicroBucket& mb = plan->buckets[static_cast<size_t>(b)];
   *info = mb.info;
   if (indices)
     for (size_t i = 0; i < mb.idx.size(); ++i) indices[i] = mb.idx[i];
+  if (offsets)
+    for (size_t i = 0; i < mb.off.size(); ++i) offsets[i] = mb.off[i];
   return MUON_OK;
+}
+
+extern "C" int64_t muon_plan_total_elems(const muon_plan_t* plan) { return plan ? plan->total : 0; }
+
+extern "C" size_t muon_workspace_bytes(const muon_shape_t* shapes, int64_t count, int32_t compute) {
+  if (count <= 0 || shapes == nullptr) return 0;
+  // one Newton-Schulz call per shape group, run one after another on one
+  // context: the largest group's need
+  size_t need = 0;
+  std::vector<char> done(static_cast<size_t>(count), 0);
+  for (int64_t i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    int64_t n = 0;
+    for (int64_t j = i; j < count; ++j)
+      if (!done[j] && same_shape(shapes[i], shapes[j])) {
+        done[j] = 1;
+        ++n;
+      }
+    const size_t w = muon_ns_workspace_bytes(shapes[i], n, compute);
+    if (w == 0) return 0;
+    need = std::max(need, w);
+  }
+  return need;
 }
 
 extern "C" size_t muon_plan_max_workspace(const muon_plan_t* plan) {

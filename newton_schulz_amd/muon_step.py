@@ -44,15 +44,13 @@ class MuonStep:
         cus = torch.cuda.get_device_properties(self.device).multi_processor_count
         self.plan = Plan(self.shapes, cap_bytes, cap_kind, compute, compute_units=cus)
 
-        # flat layout: matrices in plan order
+        # flat layout: the plan's element offsets (matrices in plan order)
         self.order: List[int] = [i for b in self.plan.buckets for i in b.indices]
         self.offset = [0] * len(self.shapes)
-        off = 0
-        for i in self.order:
-            self.offset[i] = off
-            r, c, _ = self.shapes[i]
-            off += r * c
-        self.numel = off
+        for b in self.plan.buckets:
+            for i, o in zip(b.indices, b.offsets):
+                self.offset[i] = o
+        off = self.numel = self.plan.total_elems
         dev = self.device
         self.grad = torch.zeros(off, dtype=grad_dtype, device=dev)
         self.momentum = torch.zeros(off, dtype=torch.float32, device=dev)
@@ -68,7 +66,7 @@ class MuonStep:
         self._work = []
         pos = 0
         for b in self.plan.buckets:
-            lo = self.offset[b.indices[0]]
+            lo = b.elem_offset
             hi = lo + b.numel
             groups = []
             j = 0

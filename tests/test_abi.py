@@ -7,7 +7,7 @@ import re
 import pytest
 
 from newton_schulz_amd import _lib
-from newton_schulz_amd.api import Plan, ns_workspace_bytes
+from newton_schulz_amd.api import Plan, ns_workspace_bytes, workspace_bytes
 from newton_schulz_amd import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -211,6 +211,87 @@ def test_plan_per_head_units():
     assert len(plan.buckets) == 1
     b = plan.buckets[0]
     assert (b.m, b.n, b.units, b.shape_groups) == (128, 2560, 32 + 8, 2)
+
+
+def _q4b_shapes():
+    return [(m.rows, m.cols, m.head_rows) for m in synth.qwen3_4b(layers=36).mats]
+
+
+def _shape_array(shapes):
+    return (_lib.Shape * len(shapes))(*[_lib.Shape(r, c, h) for (r, c, h) in shapes])
+
+
+def test_plan_offsets_are_the_flat_layout():
+    """muon_plan_bucket's offsets: micro-bucket after micro-bucket, members
+    packed in execution order, each micro-bucket one contiguous range."""
+    shapes = _q4b_shapes() + [(128, 2560, 0)] * 5 + [(768, 2048, 0)] * 3
+    for cus in (0, 256):
+        plan = Plan(shapes, 512 << 20, "full", "bf16", compute_units=cus)
+        pos = 0
+        for b in plan.buckets:
+            assert b.elem_offset == pos
+            assert len(b.offsets) == b.count
+            for i, o in zip(b.indices, b.offsets):
+                assert o == pos
+                pos += shapes[i][0] * shapes[i][1]
+            assert pos - b.elem_offset == b.numel
+        assert plan.total_elems == pos == sum(r * c for r, c, _ in shapes)
+
+
+def test_muon_plan_is_plan_create_bf16_greedy():
+    """muon_plan (cap and its kind only) through ctypes equals
+    muon_plan_create with BF16 compute and compute_units = 0."""
+    lib = _lib.load()
+    shapes = _q4b_shapes()
+    arr = _shape_array(shapes)
+    for cap, kind in ((512 << 20, _lib.MUON_CAP_FULL_BYTES), (1 << 30, _lib.MUON_CAP_WORKSPACE)):
+        h1, h2 = ctypes.c_void_p(), ctypes.c_void_p()
+        assert lib.muon_plan(arr, len(shapes), cap, kind, ctypes.byref(h1)) == _lib.MUON_OK
+        assert lib.muon_plan_create(arr, len(shapes), cap, kind, _lib.MUON_BF16, 0,
+                                    ctypes.byref(h2)) == _lib.MUON_OK
+        try:
+            nb = lib.muon_plan_num_buckets(h1)
+            assert nb == lib.muon_plan_num_buckets(h2) > 0
+            assert lib.muon_plan_total_elems(h1) == lib.muon_plan_total_elems(h2)
+            assert lib.muon_plan_max_workspace(h1) == lib.muon_plan_max_workspace(h2)
+            for b in range(nb):
+                i1, i2 = _lib.BucketInfo(), _lib.BucketInfo()
+                assert lib.muon_plan_bucket(h1, b, ctypes.byref(i1), None, None) == _lib.MUON_OK
+                lib.muon_plan_bucket(h2, b, ctypes.byref(i2), None, None)
+                assert bytes(i1) == bytes(i2)
+                x1, x2 = (ctypes.c_int64 * i1.count)(), (ctypes.c_int64 * i1.count)()
+                o1, o2 = (ctypes.c_int64 * i1.count)(), (ctypes.c_int64 * i1.count)()
+                lib.muon_plan_bucket(h1, b, ctypes.byref(i1), x1, o1)
+                lib.muon_plan_bucket(h2, b, ctypes.byref(i2), x2, o2)
+                assert list(x1) == list(x2) and list(o1) == list(o2)
+            info = _lib.BucketInfo()
+            assert lib.muon_plan_bucket(h1, nb, ctypes.byref(info), None, None) == _lib.MUON_EINVAL
+            assert lib.muon_plan_bucket(h1, -1, ctypes.byref(info), None, None) == _lib.MUON_EINVAL
+            assert lib.muon_plan_bucket(h1, 0, None, None, None) == _lib.MUON_EINVAL
+        finally:
+            lib.muon_plan_destroy(h1)
+            lib.muon_plan_destroy(h2)
+    assert lib.muon_plan(arr, len(shapes), 1 << 20, 7, None) == _lib.MUON_EINVAL
+    assert lib.muon_plan_total_elems(None) == 0
+    lib.muon_plan_destroy(None)
+
+
+def test_workspace_bytes_mixed_shapes():
+    """muon_workspace_bytes: the largest shape group's need (groups by exact
+    shape, wherever the members sit in the list)."""
+    shapes = [(2560, 4096, 0), (128, 2560, 0), (2560, 4096, 0), (4096, 2560, 128), (2560, 4096, 0)]
+    for compute in ("bf16", "f32"):
+        want = max(ns_workspace_bytes(2560, 4096, 3, 0, compute),
+                   ns_workspace_bytes(128, 2560, 1, 0, compute),
+                   ns_workspace_bytes(4096, 2560, 1, 128, compute))
+        assert workspace_bytes(shapes, compute) == want
+    q = _q4b_shapes()
+    groups = {}
+    for s in q:
+        groups[s] = groups.get(s, 0) + 1
+    assert workspace_bytes(q) == max(ns_workspace_bytes(r, c, n, h) for (r, c, h), n in groups.items())
+    assert workspace_bytes([]) == 0
+    assert workspace_bytes([(100, 64, 30)]) == 0
 
 
 def test_plan_rejects_bad_input():

@@ -313,8 +313,13 @@ def check_sampled(ms, w, picks, M_before, W_before, G):
         if w.mats[i].zero_grad:
             assert not np.any(dW), i
             continue
-        err = oracle.rel_fro(dW, -np.float32(w.lr) * O)
-        say(f"  {w.mats[i].name} {w.mats[i].rows}x{w.mats[i].cols}: dW rel err {err:.3e}")
+        # per Newton-Schulz unit: each head of a per-head matrix on its own
+        h = w.mats[i].head_rows or w.mats[i].rows
+        errs = [oracle.rel_fro(dW[k:k + h], -np.float32(w.lr) * O[k:k + h])
+                for k in range(0, w.mats[i].rows, h)]
+        err = max(errs)
+        say(f"  {w.mats[i].name} {w.mats[i].rows}x{w.mats[i].cols} ({len(errs)} unit(s)): "
+            f"max dW rel err {err:.3e}")
         assert err <= BF16_TOL, (i, err)
 
 
@@ -341,9 +346,12 @@ def test_qwen3_4b_full_model_sampled():
         fill_grads(ms, w, g)
         ms.momentum_only()
     fill_grads(ms, w, g)
+    # the first and last matrix of every micro-bucket, plus 8 seeded picks
     rng = np.random.default_rng(2)
-    picks = sorted({int(rng.integers(0, 7)) + 7 * int(rng.integers(0, 36)) for _ in range(3)}
-                   | {0 * 7 + 1, 35 * 7 + 3, 17 * 7 + 4, 9 * 7 + 6, 20 * 7 + 0})
+    picks = {b.indices[0] for b in ms.plan.buckets} | {b.indices[-1] for b in ms.plan.buckets}
+    picks |= {int(x) for x in rng.choice(len(w.mats), 8, replace=False)}
+    picks = sorted(picks)
+    say(f"  qwen3_4b: {len(ms.plan.buckets)} micro-buckets, {len(picks)} matrices checked")
     G = {i: host(ms.view(ms.grad, i)) for i in picks}
     M0 = {i: host(ms.view(ms.momentum, i)) for i in picks}
     W0 = {i: host(ms.view(ms.master, i)).astype(np.float64) for i in picks}
@@ -353,6 +361,7 @@ def test_qwen3_4b_full_model_sampled():
 
 
 def test_qwen3_4b_per_head_all():
+    # every one of the 1728 heads (32 q + 8 k + 8 v per layer, 36 layers)
     w = synth.qwen3_4b_heads(layers=36)
     ms, g = build_step(w)
     assert len(ms.plan.buckets) == 1 and ms.plan.buckets[0].units == 1728
@@ -363,9 +372,8 @@ def test_qwen3_4b_per_head_all():
     M0 = [np.zeros_like(x) for x in G]
     ms.step()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(3)
-    picks = sorted(set(rng.integers(0, n, 12).tolist()) | {0, n - 1})
-    check_sampled(ms, w, picks, M0, W0, G)
+    assert sum(m.rows // m.head_rows for m in w.mats) == 1728
+    check_sampled(ms, w, range(n), M0, W0, G)
 
 
 def test_moe_experts_two_layers():
