@@ -146,14 +146,18 @@ typedef struct muon_plan_s muon_plan_t;
  * MUON_EHIP (no such device / allocation failed), MUON_ENOMEM. */
 muon_status_t muon_create(int device, size_t workspace_bytes, muon_ctx_t** out);
 
-/* Free the context and its workspace.  Waits for the context's device to
- * finish the work enqueued so far.  NULL is accepted. */
+/* Free the context and its workspace (blog section "Memory control", item 2:
+ * the workspace lives as long as the context).  Waits for the context's
+ * device to finish the work enqueued so far.  NULL is accepted. */
 muon_status_t muon_destroy(muon_ctx_t* ctx);
 
-/* Size of the context's workspace slab in bytes (0 for NULL). */
+/* Size of the context's workspace slab in bytes (0 for NULL; blog section
+ * "Memory control", item 2). */
 size_t muon_ctx_workspace_bytes(const muon_ctx_t* ctx);
 
-/* Fill *p with the defaults listed above. */
+/* Fill *p with the defaults listed above (RFC section 5, Roadmap: the
+ * quintic iteration is the current default; section 2: five to six
+ * iterations). */
 void muon_ns_params_default(muon_ns_params_t* p);
 
 /* Per-iteration coefficients (RFC section 5, Roadmap: Newton-Schulz with
@@ -256,13 +260,15 @@ int64_t muon_plan_num_buckets(const muon_plan_t* plan);
  * out of range). */
 muon_status_t muon_plan_bucket(const muon_plan_t* plan, int64_t b, muon_bucket_info_t* info,
                                int64_t* indices, int64_t* offsets);
-/* Elements of the plan's flat layout (the sum of every matrix's rows x cols). */
+/* Elements of the plan's flat layout (the sum of every matrix's rows x cols;
+ * blog section "DBuffer": one persistent buffer per state). */
 int64_t muon_plan_total_elems(const muon_plan_t* plan);
 /* Largest workspace_bytes over the plan's micro-buckets: a context this large
  * runs every micro-bucket (blog section "Memory control", item 2: one
  * preallocated workspace sized by the cap). */
 size_t muon_plan_max_workspace(const muon_plan_t* plan);
-/* Free a plan (NULL is accepted). */
+/* Free a plan (NULL is accepted; blog section "Memory control": the plan is
+ * made once at init and kept). */
 void muon_plan_destroy(muon_plan_t* plan);
 
 /* ------------------------------------------------------------------------ */
@@ -287,9 +293,10 @@ muon_status_t muon_momentum_update(muon_ctx_t* ctx, void* stream, const void* gr
                                    int32_t nesterov);
 
 /* muon_momentum_update, which also leaves the sums of squares that the
- * Newton-Schulz normalisation needs (the survey's plan for the momentum step:
- * per-matrix sums of squares of U come out of the same pass, so the
- * Frobenius norms need no second read of U).  sq_partials (device,
+ * Newton-Schulz normalisation X_0 = U / (||U||_F + eps) needs (blog section
+ * "Background": Newton-Schulz runs on the refreshed momentum; the sums of
+ * squares come out of the same pass, so the Frobenius norms need no second
+ * read of U).  sq_partials (device,
  * ceil(numel / MUON_SQ_BLOCK) doubles, caller-owned) receives for block b the
  * sum of squares of update elements [b*4096, min((b+1)*4096, numel)) as
  * stored (bf16 values when update_dtype is BF16), in binary64: every square
@@ -364,8 +371,12 @@ const char* muon_noalloc_last_error(void);
 /* Diagnostics                                                               */
 /* ------------------------------------------------------------------------ */
 
+/* Static text for a status code ("unknown status" for values outside the
+ * enum).  Error reporting is part of the per-bucket diagnostics the blog's
+ * section "Metrics to record" asks for. */
 const char* muon_status_string(muon_status_t s);
-/* Text of the last error recorded on ctx (empty string when none). */
+/* Text of the last error recorded on ctx (empty string when none; NULL ctx
+ * gives a static text), blog section "Metrics to record". */
 const char* muon_last_error(const muon_ctx_t* ctx);
 
 /* Per-kernel-class timing with HIP events recorded on the launch stream
