@@ -83,11 +83,22 @@ def unit_list(w, wide_flag: bool = False):
     return units
 
 
-def traffic_record(*kernel_src: str):
+def fused_bytes(m: int, n: int, steps: int, gram: bool) -> int:
+    """HBM bytes the whole-iteration kernel must move for one m x n unit: the
+    quintic reads the input once for A_0, then per iteration reads the iterate
+    and writes the next, and the bf16 iterate's rounding residual is written
+    by iterations 0 .. steps-3 and read by iterations 1 .. steps-2; the Gram
+    form reads the input twice and writes the result once."""
+    if gram:
+        return 3 * 2 * m * n
+    return 2 * m * n * (1 + 2 * steps + 2 * max(0, steps - 2))
+
+
+def traffic_record(name: str, *kernel_src: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary, or None when missing or taken on different kernel code
-    (the kernel file and its local headers)."""
-    path = os.path.join(ROOT, "profiles", "update_kernel_traffic_qwen3_4b.json")
+    counter summary profiles/<name>.json, or None when missing or taken on
+    different kernel code (the kernel file and its local headers)."""
+    path = os.path.join(ROOT, "profiles", name + ".json")
     if not os.path.exists(path):
         return None
     from newton_schulz_amd.prof import source_fingerprint
@@ -108,6 +119,8 @@ def cpu_baseline(seconds_budget: float = 20.0, ns_steps: int = 5, minimax: bool 
         from threadpoolctl import threadpool_info, threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
+    # BLAS threads: the CPUs this process may run on, capped at 16 (the share
+    # of one GPU's host); the host's own count is reported beside it
     cores = min(len(os.sched_getaffinity(0)), 16)
     ctxm = threadpool_limits(limits=cores, user_api="blas") if threadpool_limits else None
     w = synth.qwen3_4b_layer()
@@ -156,7 +169,159 @@ def cpu_baseline(seconds_budget: float = 20.0, ns_steps: int = 5, minimax: bool 
         "sample": f"{done} of the 7 matrices of one Qwen3-4B layer (q, k, v, o, gate, up, down): "
                   f"momentum + fp64 Newton-Schulz + apply; {tot:.1f} s on the host "
                   f"(NS {t_ns:.1f} s); BLAS {blas}",
+        "blas_thread_cap": cores,
+        **host_cores(),
     }
+
+
+EXPERT_LAYER_ELEMS = 128 * 3 * 768 * 2048   # one Qwen3-30B-A3B layer's expert matrices
+EXPERT_STATE_BYTES = 2 + 4 + 4              # bf16 gradient, fp32 momentum, fp32 master
+GIB = 1 << 30
+
+
+def expert_layers_that_fit(free_bytes: int, layers: int = 48) -> int:
+    """Largest layer count (<= layers) whose expert state fits in free device
+    memory with 4 GiB to spare beyond the step's own buffers (update buffer
+    and workspace, each bounded by the 1 GiB cap)."""
+    per = EXPERT_LAYER_ELEMS * EXPERT_STATE_BYTES
+    return max(1, min(layers, (free_bytes - 4 * GIB - 2 * GIB) // per))
+
+
+def step_times(run, steps: int):
+    """Run `steps` steps between HIP events on the current stream: mean, median
+    and min ms per step, and the host wall time."""
+    import statistics
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        run()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[-1]) / steps, statistics.median(per), min(per), wall
+
+
+def host_cores():
+    return {"host_cpus": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def link_probe(dev, nbytes: int = GIB, reps: int = 3):
+    """Host<->device copy rates of `nbytes`: pinned and pageable, each
+    direction alone, and pinned both directions at once on two streams."""
+    import torch
+    d = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    d2 = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = {}
+    for pin in (True, False):
+        h = torch.ones(nbytes, dtype=torch.uint8, pin_memory=pin)
+        h2 = torch.empty(nbytes, dtype=torch.uint8, pin_memory=pin)
+        for name, fn in (("h2d", lambda: d.copy_(h, non_blocking=pin)),
+                         ("d2h", lambda: h2.copy_(d, non_blocking=pin))):
+            best = None
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
+                best = dt if best is None else min(best, dt)
+            out[f"{name}_{'pinned' if pin else 'pageable'}_GBps"] = round(nbytes / best / 1e9, 2)
+        if pin:
+            s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+            best = None
+            for _ in range(reps):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                with torch.cuda.stream(s1):
+                    d2.copy_(h, non_blocking=True)
+                with torch.cuda.stream(s2):
+                    h2.copy_(d, non_blocking=True)
+                torch.cuda.synchronize()
+                dt = time.perf_counter() - t0
+                best = dt if best is None else min(best, dt)
+            out["duplex_pinned_GBps_each_way"] = round(nbytes / best / 1e9, 2)
+        del h, h2
+    out["bytes"] = nbytes
+    return out
+
+
+def run_offload(args, w, dev):
+    """The Muon step with momentum and gradient in host memory (pinned unless
+    --pageable), `--inflight` micro-buckets on the device at a time."""
+    import torch
+    from newton_schulz_amd import synth
+    from newton_schulz_amd.offload import MuonOffloadStep
+    shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
+    t0 = time.perf_counter()
+    off = MuonOffloadStep(shapes, dev, inflight=args.inflight, pin=not args.pageable,
+                          lr=w.lr, beta=w.beta, nesterov=w.nesterov, compute=w.compute,
+                          grad_dtype=w.grad_dtype, cap_bytes=w.cap_bytes, cap_kind=w.cap_kind,
+                          ns_steps=w.ns_steps, keep_bf16_weights=True)
+    t_alloc = time.perf_counter() - t0
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    for i, W0 in enumerate(synth.iter_weights(w, g, dev)):
+        off.view(off.master, i).copy_(W0)
+    grads = [off.view(off.grad, i) for i in range(len(w.mats))]
+    for _ in range(w.warmup_momentum_steps):
+        synth.draw_grads(w, g, dev, out=grads)
+        off.momentum_only()
+    synth.draw_grads(w, g, dev, out=grads)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        off.step()
+    mean, med, mn, wall = step_times(off.step, args.steps)
+    # one more step with events around every copy and compute stage
+    off.timing = True
+    off.step()
+    torch.cuda.synchronize()
+    st = off.copy_stats()
+    off.timing = False
+    numel = off.numel
+
+    def rate(k):
+        return round(st[k]["bytes"] / (st[k]["ms"] * 1e-3) / 1e9, 2) if st[k]["ms"] > 0 else None
+
+    probe = link_probe(dev)
+    units = unit_list(w)
+    f_ns = sum(sum(ns_flops(m, n, w.ns_steps)) for (m, n) in units)
+    out = {
+        "metric": "Muon step with momentum and gradient in host memory, ms per step (Qwen3-4B shapes)",
+        "value": round(mean, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(mean, 3),
+        "ms_per_step_median": round(med, 3),
+        "ms_per_step_min": round(mn, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1e-3) bf16 gradients, fp32 state; no checkpoint)",
+        "config": {"workload": w.name + "_offload", "matrices": len(w.mats), "muon_params": numel,
+                   "inflight_micro_buckets": args.inflight, "host_memory": "pageable" if args.pageable else "pinned",
+                   "grads_on_host": True, "update_to_host": True,
+                   "micro_bucket_cap_bytes": w.cap_bytes, "micro_buckets": len(off.plan.buckets),
+                   "parallelism": "single GPU"},
+        "ns_tflops_pcie_inclusive": round(f_ns / (mean * 1e-3) / 1e12, 2),
+        "copies_per_step": {
+            "h2d_bytes": st["h2d"]["bytes"], "d2h_bytes": st["d2h"]["bytes"],
+            "h2d_ms": round(st["h2d"]["ms"], 2), "d2h_ms": round(st["d2h"]["ms"], 2),
+            "compute_ms": round(st["compute"]["ms"], 2),
+            "h2d_GBps": rate("h2d"), "d2h_GBps": rate("d2h"),
+            "pages_pinned_GBps": {"h2d": 43, "d2h": 57, "pageable": 10}},
+        "link_probe": probe,
+        "device_bytes_beyond_master": off.device_bytes(),
+        "ns_workspace_bytes": off.plan.max_workspace,
+        "host_alloc_s": round(t_alloc, 2),
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -164,7 +329,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="qwen3_4b")
+    ap.add_argument("--workload", default="qwen3_4b",
+                    help="qwen3_4b, qwen3_4b_layer, qwen3_4b_heads, qwen3_30b_experts:L "
+                         "(L layers, or 'fit': the most of 48 that fit in device memory)")
     ap.add_argument("--ns-method", default="quintic", choices=["quintic", "gram"],
                     help="Newton-Schulz evaluation; value stays the quintic's flops / step time")
     ap.add_argument("--ns-coeffs", default="fixed", choices=["fixed", "minimax"],
@@ -175,6 +342,10 @@ def main():
                     help="whole-iteration fusion of small units (muon_fuse_t)")
     ap.add_argument("--norms", default="momentum", choices=["momentum", "pass"],
                     help="Frobenius norms from the momentum pass's partials, or a separate read")
+    ap.add_argument("--offload", action="store_true",
+                    help="momentum and gradient in host memory, copied per micro-bucket")
+    ap.add_argument("--inflight", type=int, default=2, help="--offload: micro-buckets on the device")
+    ap.add_argument("--pageable", action="store_true", help="--offload: pageable host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip per-kernel event timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
@@ -198,9 +369,19 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}), flush=True)
         return
+    layers_note = None
+    if args.workload in ("qwen3_30b_experts:fit", "qwen3_30b_experts:48"):
+        free = torch.cuda.mem_get_info(dev)[0]
+        L = expert_layers_that_fit(free)
+        layers_note = {"layers_run": L, "layers_model": 48, "free_device_bytes": free,
+                       "state_bytes_per_layer": EXPERT_LAYER_ELEMS * EXPERT_STATE_BYTES}
+        args.workload = f"qwen3_30b_experts:{L}"
     w = workload_by_name(args.workload)
     if args.ns_steps:
         w = dataclasses.replace(w, ns_steps=args.ns_steps)
+    if args.offload:
+        run_offload(args, w, dev)
+        return
     shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
     keep_bf16 = not args.workload.startswith("qwen3_30b_experts")
     ms = MuonStep(shapes, dev, lr=w.lr, beta=w.beta, nesterov=w.nesterov, compute=w.compute,
@@ -209,7 +390,7 @@ def main():
                   ns_coeffs=None if args.ns_coeffs == "fixed" else args.ns_coeffs,
                   norms_from_momentum=args.norms == "momentum", ns_fuse=args.ns_fuse)
     g = torch.Generator(device=dev).manual_seed(w.seed)
-    for i, W0 in enumerate(synth.draw_weights(w, g, dev)):
+    for i, W0 in enumerate(synth.iter_weights(w, g, dev)):
         ms.view(ms.master, i).copy_(W0)
     grads = [ms.view(ms.grad, i) for i in range(len(w.mats))]
     for _ in range(w.warmup_momentum_steps):
@@ -224,18 +405,15 @@ def main():
 
     timing = not args.no_timing
     if timing:
-        ms.ctx.timing_enable(True, capacity=max(4096, args.steps * 2048))
+        # one event pair per launch: size the pool from one step's launches
+        # (launches beyond the pool would go untimed)
+        ms.ctx.timing_enable(True, capacity=1 << 14)
         ms.ctx.timing_reset()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
         ms.step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+        per = sum(v[1] for v in ms.ctx.timing_read().values())
+        ms.ctx.timing_enable(True, capacity=int(per * args.steps) + 64)
+        ms.ctx.timing_reset()
+    ms_per_step, ms_median, ms_min, wall = step_times(ms.step, args.steps)
     kt = ms.ctx.timing_read() if timing else {}
 
     units = unit_list(w)
@@ -250,6 +428,7 @@ def main():
     # use the flops each class actually executed
     value = f_ns / (ms_per_step * 1e-3) / 1e12
     ex = {"gram": 0, "symsq": 0, "prod": 0, "update": 0, "fused": 0}
+    fused_hbm = 0
     # units the library ran as one fused launch (small wide bf16 units; every
     # such call in these workloads has a unit per CU)
     fused_ran = timing and kt["fused"][1] > 0
@@ -260,6 +439,7 @@ def main():
             (fg, fs, fu), fp = ns_flops(m, n, w.ns_steps), 0
         if fused_ran and w.compute == "bf16" and wide and m <= 128:
             ex["fused"] += fg + fs + fp + fu
+            fused_hbm += fused_bytes(m, n, w.ns_steps, args.ns_method == "gram")
             continue
         ex["gram"] += fg
         ex["symsq"] += fs
@@ -293,18 +473,37 @@ def main():
             t = per_step[k][0]
             breakdown[k]["gbs"] = round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
             breakdown[k]["frac_hbm"] = round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if t > 0 else None
-        t_upd, n_upd = per_step["update"]
-        f_upd = ex["update"]
-        if n_upd > 0 and t_upd > 0:
-            achieved = f_upd / (t_upd * 1e-3) / 1e12
-            csrc = os.path.join(ROOT, "newton_schulz_amd", "csrc")
-            traffic = traffic_record(os.path.join(csrc, "ns_gemm_mfma.hip"),
-                                     os.path.join(csrc, "ns_mfma_common.h"))
+        # the dominant Newton-Schulz kernel class by time
+        dom = max(("gram", "symsq", "prod", "update", "fused"), key=lambda k: per_step[k][0])
+        t_dom, n_dom = per_step[dom]
+        csrc = os.path.join(ROOT, "newton_schulz_amd", "csrc")
+        if dom == "fused" and t_dom > 0:
+            achieved = fused_hbm / (t_dom * 1e-3) / 1e9
+            breakdown["fused"]["gbs"] = round(achieved, 1)
+            traffic = traffic_record(f"ns_small_kernel_traffic_{w.name}",
+                                     os.path.join(csrc, "ns_small.hip"), os.path.join(csrc, "ns_mfma_common.h"))
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                        "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                        "kernel": "ns_small_kernel (every iteration of units with m <= 128 in one launch)",
+                        "avg_launch_ms": round(t_dom / n_dom, 4),
+                        "bytes_per_launch_avg": int(fused_hbm / n_dom),
+                        "mfma_tflops": breakdown["fused"].get("tflops"),
+                        "mfma_frac": round(breakdown["fused"]["tflops"] / PEAK_BF16_TFLOPS, 4)
+                        if breakdown["fused"].get("tflops") else None}
+        elif n_dom > 0 and t_dom > 0:
+            achieved = ex[dom] / (t_dom * 1e-3) / 1e12
+            traffic = None
+            if dom == "update":
+                traffic = traffic_record(f"update_kernel_traffic_{w.name}",
+                                         os.path.join(csrc, "ns_gemm_mfma.hip"),
+                                         os.path.join(csrc, "ns_mfma_common.h"))
+            what = {"update": "update X' = B' X, B' = a I + b A + c A A", "gram": "Gram A = X X^T",
+                    "symsq": "B' = a I + b A + c A A", "prod": "m x m products of the Gram form"}[dom]
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                        "traffic": traffic, "kernel": "ns_gemm_mfma_kernel (update X' = B' X, B' = a I + b A + c A A)",
-                        "avg_launch_ms": round(t_upd / n_upd, 4),
-                        "flop_per_launch_avg": int(f_upd / n_upd)}
+                        "traffic": traffic, "kernel": f"ns_gemm_mfma_kernel ({what})",
+                        "avg_launch_ms": round(t_dom / n_dom, 4),
+                        "flop_per_launch_avg": int(ex[dom] / n_dom)}
 
     out = {
         "metric": METRIC if args.ns_method == "quintic" else METRIC.replace(
@@ -315,6 +514,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(ms_median, 4),
+        "ms_per_step_min": round(ms_min, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -336,6 +537,15 @@ def main():
         "breakdown": breakdown,
         "roofline": roofline,
     }
+    if layers_note is not None:
+        L = layers_note["layers_run"]
+        if L < 48:
+            layers_note["ms_per_step_x48_over_L"] = round(ms_per_step * 48 / L, 2)
+            layers_note["note"] = (f"{L} of the 48 layers fit in device memory; the 48-layer step time "
+                                   f"is extrapolated as x48/{L}, not measured")
+        else:
+            layers_note["note"] = "all 48 layers measured"
+        out["layers"] = layers_note
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(ns_steps=w.ns_steps, minimax=args.ns_coeffs == "minimax")
     print(json.dumps(out), flush=True)

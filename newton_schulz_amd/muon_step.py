@@ -50,20 +50,28 @@ class MuonStep:
         for b in self.plan.buckets:
             for i, o in zip(b.indices, b.offsets):
                 self.offset[i] = o
-        off = self.numel = self.plan.total_elems
-        dev = self.device
+        self.numel = self.plan.total_elems
+        self.max_bucket = max((b.numel for b in self.plan.buckets), default=0)
+        self.norms_from_momentum = norms_from_momentum
+        self.ctx = Context(self.device, self.plan.max_workspace)
+        self._alloc_state(grad_dtype, keep_bf16_weights)
+
+    def _alloc_state(self, grad_dtype: torch.dtype, keep_bf16_weights: bool):
+        off, dev = self.numel, self.device
         self.grad = torch.zeros(off, dtype=grad_dtype, device=dev)
         self.momentum = torch.zeros(off, dtype=torch.float32, device=dev)
         self.master = torch.zeros(off, dtype=torch.float32, device=dev)
         self.weight_bf16 = torch.zeros(off, dtype=torch.bfloat16, device=dev) if keep_bf16_weights else None
-        max_bucket = max((b.numel for b in self.plan.buckets), default=0)
-        self.update = torch.empty(max(max_bucket, 1), dtype=self.cdtype, device=dev)
+        self.update = torch.empty(max(self.max_bucket, 1), dtype=self.cdtype, device=dev)
         # per-4096-element sums of squares of the update, from the momentum pass
-        self.sq = torch.empty(max(sq_blocks(max_bucket), 1), dtype=torch.float64, device=dev)
-        self.ctx = Context(dev, self.plan.max_workspace)
+        self.sq = torch.empty(max(sq_blocks(self.max_bucket), 1), dtype=torch.float64, device=dev)
+        self._work = self._bucket_work(self.update)
 
-        # per micro-bucket: element range and shape groups with cached pointer arrays
-        self._work = []
+    def _bucket_work(self, update: torch.Tensor):
+        """Per micro-bucket: its element range and its shape groups, each with
+        views of `update` (the micro-bucket laid out from its start) and the
+        cached pointer arrays of those views."""
+        work = []
         pos = 0
         for b in self.plan.buckets:
             lo = b.elem_offset
@@ -75,17 +83,19 @@ class MuonStep:
                 while k < len(b.indices) and self.shapes[b.indices[k]] == self.shapes[b.indices[j]]:
                     k += 1
                 r, c, h = self.shapes[b.indices[j]]
-                mats = [self._uview(self.offset[i] - lo, r, c) for i in b.indices[j:k]]
+                rel = [self.offset[i] - lo for i in b.indices[j:k]]
+                mats = [update[o:o + r * c].view(r, c) for o in rel]
                 # norms from the momentum partials when every unit of the group
                 # starts on, and spans, whole 4096-element blocks
                 unit = (h if h else r) * c
-                whole = norms_from_momentum and unit % SQ_BLOCK == 0 and all(
-                    (self.offset[i] - lo) % SQ_BLOCK == 0 for i in b.indices[j:k])
+                whole = self.norms_from_momentum and unit % SQ_BLOCK == 0 and all(
+                    o % SQ_BLOCK == 0 for o in rel)
                 groups.append((h, mats, self.ctx.pointer_arrays(mats), whole))
                 j = k
-            self._work.append((lo, hi, groups, any(g[3] for g in groups)))
+            work.append((lo, hi, groups, any(g[3] for g in groups)))
             pos = hi
         assert pos == self.numel
+        return work
 
     def _uview(self, off: int, r: int, c: int) -> torch.Tensor:
         return self.update[off:off + r * c].view(r, c)
@@ -102,13 +112,22 @@ class MuonStep:
             self.ctx.momentum_update(self.grad[lo:hi], self.momentum[lo:hi], self.update[:hi - lo],
                                      self.beta, self.nesterov, stream)
 
+    def _run_bucket(self, grad, momentum, upd, sq, groups, want_sq, master, wb, stream, flag):
+        """momentum -> Newton-Schulz per shape group -> apply, for one
+        micro-bucket whose update buffer `upd` is laid out as in _bucket_work."""
+        self.ctx.momentum_update(grad, momentum, upd, self.beta, self.nesterov, stream,
+                                 sq_partials=sq if want_sq else None)
+        self._run_nsa(upd, sq, groups, master, wb, stream, flag)
+
+    def _run_nsa(self, upd, sq, groups, master, wb, stream, flag):
+        """Newton-Schulz per shape group, in place on `upd`, then the apply."""
+        for h, mats, ptrs, whole in groups:
+            self.ctx.newton_schulz(mats, None, h, self.params, flag, stream, _ptrs=ptrs,
+                                   sq=(sq, upd) if whole else None)
+        self.ctx.apply(master, upd, self.lr, self.scale, self.weight_decay, wb, stream)
+
     def step(self, stream=None, nonfinite_flag: Optional[torch.Tensor] = None):
         for lo, hi, groups, want_sq in self._work:
-            upd = self.update[:hi - lo]
-            self.ctx.momentum_update(self.grad[lo:hi], self.momentum[lo:hi], upd, self.beta,
-                                     self.nesterov, stream, sq_partials=self.sq if want_sq else None)
-            for h, mats, ptrs, whole in groups:
-                self.ctx.newton_schulz(mats, None, h, self.params, nonfinite_flag, stream, _ptrs=ptrs,
-                                       sq=(self.sq, upd) if whole else None)
             wb = self.weight_bf16[lo:hi] if self.weight_bf16 is not None else None
-            self.ctx.apply(self.master[lo:hi], upd, self.lr, self.scale, self.weight_decay, wb, stream)
+            self._run_bucket(self.grad[lo:hi], self.momentum[lo:hi], self.update[:hi - lo], self.sq,
+                             groups, want_sq, self.master[lo:hi], wb, stream, nonfinite_flag)

@@ -153,8 +153,15 @@ def draw_grads(w: Workload, gen: torch.Generator, device, out: Optional[List[tor
     return res
 
 
+def iter_weights(w: Workload, gen: torch.Generator, device):
+    """The fp32 master weights one matrix at a time, in workload order (the
+    draws of draw_weights, without holding them all)."""
+    for m in w.mats:
+        yield normal((m.rows, m.cols), w.weight_std, gen, device, torch.float32)
+
+
 def draw_weights(w: Workload, gen: torch.Generator, device):
-    return [normal((m.rows, m.cols), w.weight_std, gen, device, torch.float32) for m in w.mats]
+    return list(iter_weights(w, gen, device))
 
 
 # Spectra that Gaussian draws do not reach.  Newton-Schulz lifts every

@@ -108,3 +108,24 @@ def test_qwen3_4b_muon_parameters_match_the_pages():
     assert round((params - 3 * 2560 * (9728 - 9216) * 36) * 4 / 1e9, 1) != g["total_gb"]
     assert round(params * 35 / 36 * 4 / 1e9, 1) != g["total_gb"]
     assert round((params + 2 * 2560 * (2560 - 1024) * 36) * 4 / 1e9, 1) != g["total_gb"]
+
+
+def test_fused_bytes_count_the_iterate_and_residual_passes():
+    # quintic, 5 iterations: the input once for A_0, then 5 reads and 5
+    # writes of the iterate, and the residual written by iterations 0..2
+    # and read by iterations 1..3: 17 passes of 2 m n bytes
+    assert bench.fused_bytes(128, 2560, 5, gram=False) == 17 * 2 * 128 * 2560
+    # two iterations carry no residual: input + 2 reads + 2 writes
+    assert bench.fused_bytes(128, 2560, 2, gram=False) == 5 * 2 * 128 * 2560
+    assert bench.fused_bytes(128, 2560, 3, gram=False) == 9 * 2 * 128 * 2560
+    # the Gram form reads the input twice and writes once
+    assert bench.fused_bytes(96, 4096, 5, gram=True) == 3 * 2 * 96 * 4096
+
+
+def test_expert_layers_that_fit():
+    per = 128 * 3 * 768 * 2048 * 10
+    gib = 1 << 30
+    assert bench.expert_layers_that_fit(48 * per + 6 * gib) == 48
+    assert bench.expert_layers_that_fit(10 ** 15) == 48
+    assert bench.expert_layers_that_fit(45 * per + 6 * gib + per - 1) == 45
+    assert bench.expert_layers_that_fit(0) == 1
