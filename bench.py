@@ -59,6 +59,8 @@ def workload_by_name(name):
     from newton_schulz_amd import synth
     if name == "qwen3_4b":
         return synth.qwen3_4b()
+    if name == "tiny":
+        return synth.tiny()
     if name == "qwen3_4b_layer":
         return synth.qwen3_4b_layer()
     if name == "qwen3_4b_heads":
@@ -249,6 +251,42 @@ def link_probe(dev, nbytes: int = GIB, reps: int = 3):
     return out
 
 
+def run_library_gemm(args, w, dev):
+    """The vendor library's batched GEMM (torch.bmm -> hipBLASLt) on the
+    products of one Newton-Schulz iteration, per canonical unit shape, with
+    the batch of the workload's largest micro-bucket of that shape: the update
+    B'X (m x m times m x n) and the Gram X X^T (dense: the library computes
+    both triangles).  Random bf16 operands (the MFMA rate depends on the
+    data); transposed operands are made contiguous first."""
+    import torch
+    from newton_schulz_amd.api import Plan
+    shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
+    plan = Plan(shapes, w.cap_bytes, w.cap_kind, w.compute)
+    batch = {}
+    for b in plan.buckets:
+        batch[(b.m, b.n)] = max(batch.get((b.m, b.n), 0), b.units)
+    dt = torch.bfloat16 if w.compute == "bf16" else torch.float32
+    g = torch.Generator(device=dev).manual_seed(0)
+    rows = []
+    for (m, n), U in batch.items():
+        X = torch.randn((U, m, n), generator=g, device=dev).to(dt)
+        B = torch.randn((U, m, m), generator=g, device=dev).to(dt)
+        Xt = X.transpose(1, 2).contiguous()
+        res = {"m": m, "n": n, "batch": U}
+        for name, fn, flops in (("update", lambda: torch.bmm(B, X), 2 * m * m * n * U),
+                                ("gram", lambda: torch.bmm(X, Xt), 2 * m * m * n * U)):
+            for _ in range(3):
+                fn()
+            mean, med, mn, _ = step_times(fn, max(args.steps, 5))
+            res[name] = {"ms_median": round(med, 4), "tflops_median": round(flops / (med * 1e-3) / 1e12, 1),
+                         "tflops_best": round(flops / (mn * 1e-3) / 1e12, 1)}
+        rows.append(res)
+        del X, B, Xt
+    print(json.dumps({"library_gemm": "torch.bmm (hipBLASLt), dense flops 2 m^2 n per product",
+                      "dtype": w.compute, "workload": w.name, "shapes": rows,
+                      "torch": torch.__version__}), flush=True)
+
+
 def run_offload(args, w, dev):
     """The Muon step with momentum and gradient in host memory (pinned unless
     --pageable), `--inflight` micro-buckets on the device at a time."""
@@ -342,6 +380,11 @@ def main():
                     help="whole-iteration fusion of small units (muon_fuse_t)")
     ap.add_argument("--norms", default="momentum", choices=["momentum", "pass"],
                     help="Frobenius norms from the momentum pass's partials, or a separate read")
+    ap.add_argument("--compute", default=None, choices=["bf16", "f32"],
+                    help="override the workload's Newton-Schulz compute mode (f32: verification mode)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="instead of the step: the vendor library's batched GEMM (torch.bmm) on the "
+                         "Newton-Schulz products of the workload's micro-buckets, as a yardstick")
     ap.add_argument("--offload", action="store_true",
                     help="momentum and gradient in host memory, copied per micro-bucket")
     ap.add_argument("--inflight", type=int, default=2, help="--offload: micro-buckets on the device")
@@ -379,6 +422,11 @@ def main():
     w = workload_by_name(args.workload)
     if args.ns_steps:
         w = dataclasses.replace(w, ns_steps=args.ns_steps)
+    if args.compute:
+        w = dataclasses.replace(w, compute=args.compute)
+    if args.library_gemm:
+        run_library_gemm(args, w, dev)
+        return
     if args.offload:
         run_offload(args, w, dev)
         return
@@ -519,7 +567,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": w.compute,
         "data": "synthetic (seeded N(0,1e-3) bf16 gradients, fp32 state; no checkpoint)",
         "config": {"workload": w.name, "matrices": len(w.mats), "muon_params": numel,
                    "ns_units": len(units), "ns_steps": w.ns_steps, "ns_method": args.ns_method,

@@ -175,9 +175,12 @@ void muon_ns_params_default(muon_ns_params_t* p);
  * polynomial (15/8, -5/4, 3/8).  Pure host function, computed in double.
  * out: `steps` x 3 floats (caller-owned, host).  *bound (may be NULL)
  * receives E_{steps-1}: in exact arithmetic every singular value of X_0 in
- * [lo, 1] ends within [1 - bound, 1 + bound].  Errors: MUON_EINVAL (steps < 1
- * or > 1024, lo outside (0, 1), margin outside [0, 0.5], out NULL, or the
- * exchange did not converge). */
+ * [lo, 1] ends within [1 - bound, 1 + bound].  `margin` must lie in [0.01, 0.1]:
+ * with bf16 iterates, low-rank inputs reached relative errors of 0.36 at
+ * margin 0 and 0.14 at margin 0.2 against the fp64 iteration with the same
+ * coefficients, and stayed within 2e-2 inside that window.  Errors:
+ * MUON_EINVAL (steps < 1 or > 1024, lo outside (0, 1), margin outside
+ * [0.01, 0.1], out NULL, or the exchange did not converge). */
 muon_status_t muon_ns_minimax_coeffs(int32_t steps, double lo, double margin, float* out,
                                      double* bound);
 

@@ -104,8 +104,12 @@ bool best_quintic(double lo, double hi, Quintic* best, double* err) {
 
 extern "C" muon_status_t muon_ns_minimax_coeffs(int32_t steps, double lo, double margin,
                                                 float* out, double* bound) {
+  // margins outside [0.01, 0.1] are refused: with bf16 iterates, low-rank
+  // inputs measured a relative error of 0.36 at margin 0 (values that
+  // rounding pushes past the top of the interval meet the polynomial's steep
+  // rise) and up to 0.14 at margin 0.2 (a wider interval, a coarser fit)
   if (out == nullptr || steps < 1 || steps > 1024 || !(lo > 0.0 && lo < 1.0) ||
-      !(margin >= 0.0 && margin <= 0.5))
+      !(margin >= 0.01 && margin <= 0.1))
     return MUON_EINVAL;
   // As the interval shrinks to {1} the best polynomial tends to the one that
   // matches 1 to third order there: p(1) = 1, p'(1) = p''(1) = 0, i.e.

@@ -303,7 +303,7 @@ def test_plan_rejects_bad_input():
 
 
 @pytest.mark.parametrize("steps,lo,margin", [
-    (1, 1e-3, 0.02), (6, 1e-3, 0.02), (10, 1e-3, 0.0), (5, 0.1, 0.05), (3, 0.5, 0.0), (8, 1e-4, 0.2),
+    (1, 1e-3, 0.02), (6, 1e-3, 0.02), (10, 1e-3, 0.01), (5, 0.1, 0.05), (3, 0.5, 0.01), (8, 1e-4, 0.1),
 ])
 def test_minimax_coeffs_match_oracle(steps, lo, margin):
     """libmuon's host schedule against the oracle's own (independent) one."""
@@ -321,8 +321,11 @@ def test_minimax_coeffs_rejects_bad_arguments():
     out = (ctypes.c_float * 30)()
     ok = lib.muon_ns_minimax_coeffs(10, 1e-3, 0.02, out, None)
     assert ok == _lib.MUON_OK
+    # margins outside [0.01, 0.1] are refused (measured to diverge with bf16
+    # iterates on low-rank inputs), though the schedule itself is defined
     for steps, lo, margin in [(0, 1e-3, 0.02), (1025, 1e-3, 0.02), (3, 0.0, 0.02), (3, 1.0, 0.02),
-                              (3, float("nan"), 0.02), (3, 1e-3, -0.01), (3, 1e-3, 0.51),
+                              (3, float("nan"), 0.02), (3, 1e-3, -0.01), (3, 1e-3, 0.0),
+                              (3, 1e-3, 0.009), (3, 1e-3, 0.11), (3, 1e-3, 0.2),
                               (3, 1e-3, float("nan"))]:
         assert lib.muon_ns_minimax_coeffs(steps, lo, margin, out, None) == _lib.MUON_EINVAL
     assert lib.muon_ns_minimax_coeffs(3, 1e-3, 0.02, None, None) == _lib.MUON_EINVAL

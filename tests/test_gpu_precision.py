@@ -10,7 +10,7 @@ rank 8 over a noise floor 1e-3 below it, and a geometric spectrum over six
 decades -- to the same bar as the Gaussian draws: relative Frobenius error
 <= 2e-2 against the fp64 oracle on the same bf16 values.  The bf16 path
 meets it by carrying the iterate's rounding residual between iterations and
-completing B's diagonal in fp32 (ns_diag_correct); storing the iterate in
+completing B's diagonal in fp32 (ns_diag_residual, ns_lo_term); storing the iterate in
 bf16 alone misses it by an order of magnitude on the low-rank inputs.
 """
 import sys
@@ -99,6 +99,21 @@ def test_minimax(ctx, r, c, kind, scale):
     outs = run(ctx, y, ns_params(coeffs="minimax"), count=1)
     err = oracle.rel_fro(outs[0], ref)
     say(f"  minimax {r}x{c} {kind} x{scale:g}: rel err {err:.3e}")
+    assert err <= BF16_TOL
+
+
+@pytest.mark.parametrize("r,c", [(2560, 4096), (768, 2048)])
+@pytest.mark.parametrize("kind", ["rank1", "rank8_noise", "geometric"])
+@pytest.mark.parametrize("margin", [0.01, 0.1])
+def test_minimax_margin_window(ctx, r, c, kind, margin):
+    # the ends of the margin window muon_ns_minimax_coeffs accepts
+    from newton_schulz_amd import minimax_coeffs
+    rows, _ = minimax_coeffs(5, 1e-3, margin)
+    y = synth.structured(kind, r, c, seed=r + c)
+    ref = oracle.ns_ref(y.float().numpy().astype(np.float64), coeffs=np.array(rows, dtype=np.float64))
+    outs = run(ctx, y, ns_params(coeffs=rows), count=1)
+    err = oracle.rel_fro(outs[0], ref)
+    say(f"  minimax margin {margin} {r}x{c} {kind}: rel err {err:.3e}")
     assert err <= BF16_TOL
 
 
