@@ -14,17 +14,22 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
 }
 
 // fp32 -> bf16, round to nearest, ties to even; NaN stays a quiet NaN;
-// overflow rounds to infinity.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
-}
+// overflow rounds to infinity.  On the bit pattern u: a NaN gives
+// (u >> 16) | 0x40, anything else the high half of u + 0x7fff + ((u >> 16) & 1).
+// gfx950 does this in one instruction, v_cvt_pk_bf16_f32 (two values at a
+// time): on an MI355X its result equals that rule for every one of the 2^32
+// inputs, NaN payloads included, so the kernels use it.
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
 
 // Two fp32 values -> packed pair of bf16 (lo in bits 0..15).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const f32x2_cvt v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_cvt));
+}
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  return static_cast<bf16_t>(pack_bf16x2(f, 0.0f));
 }
 
 template <typename T> struct Elem;
@@ -35,14 +40,14 @@ __device__ __forceinline__ float bf16_round(float f) { return bf16_to_f32(f32_to
 // The bf16 iteration with the iterate carried past bf16.  The iterate is
 // X = hi + lo: hi the stored bf16 matrix the products read, lo its rounding
 // residual (kept in a plane of its own).  The MFMA applies B' with its
-// diagonal d rounded to bf16, so it sums (B'_bf16 hi)_ij; the diagonal's exact
-// contribution d X_ij = bf16(d) hi + (d - bf16(d)) hi + d lo is completed in
-// fp32: r hi (r = ns_diag_residual(d)) is added to the accumulator just
-// before the MFMAs of the k-stage holding row i (wide; column j when tall),
-// d lo after the last one (ns_lo_term).  Without this, the small singular
-// values that the iteration lifts by up to a^steps are lost in the bf16
-// storage of X.  Every kernel computing it keeps this order (no contraction),
-// so they give the same bits.
+// diagonal d rounded to bf16, so it sums (B'_bf16 hi)_ij; the diagonal's
+// contribution d X_ij = bf16(d) hi + (d - bf16(d)) hi + d lo is completed:
+// r hi (r = ns_diag_residual(d), rounded to bf16) as one more MFMA against a
+// diagonal operand in the k-step that contracts over row i (wide; column j
+// when tall), d lo after the last MFMA (ns_lo_term).  Without this, the
+// small singular values that the iteration lifts by up to a^steps are lost in
+// the bf16 storage of X.  Every kernel computing it keeps this order (no
+// contraction), so they give the same bits.
 __device__ __forceinline__ float ns_diag_residual(float d) { return d - bf16_round(d); }
 __device__ __forceinline__ float ns_lo_term(float acc, float d, float lo) { return acc + d * lo; }
 

@@ -258,62 +258,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     mirror_lower(d, tid);
     barrier_lds();
   };
-  // xd = f B xs (B in bp) block by block through the staging tile am; with
-  // `next`, an accumulates xd xd^T from the stored bf16 blocks.  With dg set
-  // (quintic), B's fp32 diagonal is completed and the iterate's residual
-  // carried (ns_diag_residual, ns_lo_term): lo_in / lo_out are the unit's residual planes
-  // (one 32 KiB block per column block, each lane's values of a 32-row block
-  // as four contiguous chunks; lo_in null for the exact bf16 input, lo_out
-  // null when not kept).
-  auto column_pass = [&](const bf16_t* xs, const bf16_t* xd, float f, bool next, Acc& an,
-                         const float* dg, const char* lo_in, char* lo_out) {
-    float drow[2] = {0.0f, 0.0f};
-    if (dg != nullptr) {
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi) {
-        const int i = wm * 64 + mi * 32 + (lane & 31);
-        if (i < m) drow[mi] = dg[i];
-      }
-    }
-    auto lo_chunk = [&](const char* plane, int c, int ch) {
-      return const_cast<char*>(plane) + static_cast<int64_t>(c) * SLAB + (ch * NWV + wave) * 1024 +
-             lane * 16;
-    };
-    const u32x4_t rs = rsrc_words(xs, ubytes);
-    uint32_t base[NGC];
-    int cc[NGC];
-#pragma unroll
-    for (int q = 0; q < NGC; ++q) {
-      const int kr = 4 * (wave + NWV * q) + (lane >> 4);
-      const int col = 8 * ((lane & 15) ^ ((kr & 3) << 2));
-      cc[q] = col;
-      base[q] = kr < m ? static_cast<uint32_t>((static_cast<int64_t>(kr) * n + col) * 2) : kOOB;
-    }
-    auto issue = [&](char* sl, int c0) {
-      dma16_group<NGC>(
-          rs, static_cast<uint32_t>(c0 * 2), [&](int q) { return sl + (wave + NWV * q) * 1024; },
-          [&](int q) { return c0 + cc[q] < n ? base[q] : kOOB; });
-    };
-    an.zero();
-    issue(s0, 0);
-    issue(s1, SM);
-    issue(s2, 2 * SM);
-    for (int c = 0; c < nb; ++c) {
-      char* sl = (c % 3 == 0) ? s0 : ((c % 3 == 1) ? s1 : s2);
-      // wait for this wave's block-c loads; issued after them: blocks c + 1,
-      // c + 2 (8 loads each) and the stores of blocks c - 2, c - 1 (8 each).
-      // With the residual, the loads and stores of the residual blocks come
-      // in between too: wait for everything (the count would depend on the
-      // residual's presence; this path is not the bandwidth-critical one).
-      if (dg != nullptr)
-        asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-      else if (c == 0)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC) : "memory");
-      else if (c == 1)
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC + NST) : "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC + 2 * NST) : "memory");
-      Acc ax;
+  // ax = B' X_c for the K-major iterate block in sl (B' in bp); with diag,
+  // B's diagonal residual r (bf16) on the 16 rows each step contracts over,
+  // as one more MFMA per accumulator of their 32-row block: the same operand
+  // and order as the 128-tile launches
+  auto block_product = [&](const char* sl, Acc& ax, bool diag, const float (&drow)[2]) {
       ax.zero();
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
@@ -324,10 +273,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
           fb[i] = rt_frag(bp, wm * 64 + i * 32, kk, lane);
         }
         ax.mma(fa, fb);
-        // B's diagonal residual r (bf16) on the 16 rows this step contracts
-        // over, as one more MFMA per accumulator of their 32-row block: the
-        // same operand and order as the 128-tile launches
-        if (dg != nullptr && (kk >> 2) == wm) {
+        if (diag && (kk >> 2) == wm) {
           const int mis = (kk >> 1) & 1;
           const int idx = wm * 64 + mis * 32 + (lane & 31);
           const int e = idx - 16 * kk - 8 * (lane >> 5);
@@ -347,55 +293,182 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
           }
         }
       }
-      if (dg == nullptr) {
+  };
+  // The column pass of the quintic with B's fp32 diagonal and the iterate's
+  // residual (dg set): iterate blocks alternate between s0 and s1, residual
+  // blocks between s2 and am, and each X' block is staged in the slab its
+  // input block came in (free once its product is done), so one block of
+  // each is always in flight.  Residual blocks come in by global->LDS DMA in
+  // the plane's byte order, every wave fetching the 1 KiB pieces it reads
+  // back itself (piece q of wave w at (w + NWV q) KiB: its chunk q), so no
+  // register load queues behind the DMA in flight.  At the top of block c,
+  // issued after its loads: the residual and X' stores of block c - 1 and
+  // the loads of block c + 1 (both kinds of memory operation count, in issue
+  // order) -- the wait counts below.
+  auto column_pass_res = [&](const bf16_t* xd, float f, bool next, Acc& an, const float (&drow)[2],
+                             const char* lo_in, char* lo_out, auto&& issue_x) {
+    const u32x4_t lrs = rsrc_words(lo_in ? lo_in : lo_out, static_cast<uint32_t>(nb) * SLAB);
+    auto issue_lo = [&](char* buf, int c) {
+      if (lo_in == nullptr) return;
+      dma16_group<8>(
+          lrs, static_cast<uint32_t>(c) * SLAB, [&](int q) { return buf + (wave + NWV * q) * 1024; },
+          [&](int q) { return c < nb ? static_cast<uint32_t>((wave + NWV * q) * 1024 + lane * 16) : kOOB; });
+    };
+    auto slab = [&](int c) { return (c & 1) ? s1 : s0; };
+    auto lobuf = [&](int c) { return (c & 1) ? am : s2; };
+    // memory operations per wave: NGC per iterate block, 8 per residual
+    // block, NST X' stores and 8 residual stores per block
+    constexpr int NLO = 8, NLS = 8;
+    static_assert(NGC == 8 && NST == 8, "wait counts below assume 8 operations per group");
+    const int n_in = (lo_in ? NLO : 0) + NGC;
+    const int n_out = (lo_out ? NLS : 0) + NST;
+    issue_lo(lobuf(0), 0);
+    issue_x(slab(0), 0);
+    issue_lo(lobuf(1), 1);
+    issue_x(slab(1), SM);
+    for (int c = 0; c < nb; ++c) {
+      char* sl = slab(c);
+      const int nw = (c == 0 ? 0 : n_out) + n_in;  // 8 .. 32, a multiple of 8
+      if (nw == 8)
+        asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+      else if (nw == 16)
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+      else if (nw == 24)
+        asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
+      Acc ax;
+      block_product(sl, ax, true, drow);
+      // this wave's residual chunks of block c, from the pieces it fetched
+      u32x4_t lov[8];
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch)
+        lov[ch] = lo_in ? *reinterpret_cast<const u32x4_t*>(lobuf(c) + (ch * NWV + wave) * 1024 + lane * 16)
+                        : u32x4_t{0u, 0u, 0u, 0u};
+      barrier_lds();  // every wave is done reading block c: stage X' over it
+      static_for<2>([&](auto MI) {
+        constexpr int mi = decltype(MI)::value;
+        u32x4_t lon[4];
+        static_for<2>([&](auto NI) {
+          static_for<4>([&](auto G) {
+            constexpr int ni = decltype(NI)::value, g = decltype(G)::value;
+            const int i = wm * 64 + mi * 32 + (lane & 31);
+            const int j = wn * 64 + ni * 32 + 8 * g + 4 * (lane >> 5);
+            const u32x4_t lc = lov[mi * 4 + 2 * ni + g / 2];
+            const uint32_t l0 = (g & 1) ? lc.z : lc.x, l1 = (g & 1) ? lc.w : lc.y;
+            const float lo[4] = {__uint_as_float(l0 << 16), __uint_as_float(l0 & 0xffff0000u),
+                                 __uint_as_float(l1 << 16), __uint_as_float(l1 & 0xffff0000u)};
+            float v[4], r[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              v[q] = ax.v[mi][ni][4 * g + q];
+              if (lo_in) v[q] = muon::ns_lo_term(v[q], drow[mi], lo[q]);
+              v[q] = f * v[q];
+              r[q] = v[q] - muon::bf16_round(v[q]);
+            }
+            u32x4_t& lw = lon[2 * ni + g / 2];
+            if (g & 1) {
+              lw.z = muon::pack_bf16x2(r[0], r[1]);
+              lw.w = muon::pack_bf16x2(r[2], r[3]);
+            } else {
+              lw.x = muon::pack_bf16x2(r[0], r[1]);
+              lw.y = muon::pack_bf16x2(r[2], r[3]);
+            }
+            *reinterpret_cast<uint2*>(rt_at(sl, i, j)) = pack4(v);
+          });
+        });
+        if (lo_out) {
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch)
+            __builtin_nontemporal_store(
+                lon[ch], reinterpret_cast<u32x4_t*>(lo_out + static_cast<int64_t>(c) * SLAB +
+                                                    ((mi * 4 + ch) * NWV + wave) * 1024 + lane * 16));
+        }
+      });
+      barrier_lds();
+      store_block(xd, c * SM, sl);
+      if (next) {
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk) {
+          bf16x8_t fa[2], fb[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            fa[i] = rt_frag(sl, wn * 64 + i * 32, kk, lane);
+            fb[i] = rt_frag(sl, wm * 64 + i * 32, kk, lane);
+          }
+          an.mma(fa, fb);
+        }
+      }
+      barrier_lds();  // block c's slab and residual buffer are free again
+      issue_lo(lobuf(c), c + 2);
+      issue_x(sl, (c + 2) * SM);
+    }
+    // whatever reads this pass's output next sees every store, and the
+    // zero-filling loads issued past the last block have landed
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  };
+  // xd = f B xs (B in bp) block by block; with `next`, an accumulates
+  // xd xd^T from the stored bf16 blocks.  With dg set (quintic), B's fp32
+  // diagonal is completed and the iterate's residual carried
+  // (ns_diag_residual, ns_lo_term) in column_pass_res: lo_in / lo_out are the
+  // unit's residual planes (one 32 KiB block per column block, each lane's
+  // values of a 32-row block as four contiguous 16-byte chunks; lo_in null
+  // for the exact bf16 input, lo_out null when not kept).  Without dg, three
+  // iterate blocks rotate through s0 .. s2 and X' is staged in am.
+  auto column_pass = [&](const bf16_t* xs, const bf16_t* xd, float f, bool next, Acc& an,
+                         const float* dg, const char* lo_in, char* lo_out) {
+    float drow[2] = {0.0f, 0.0f};
+    if (dg != nullptr) {
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) {
+        const int i = wm * 64 + mi * 32 + (lane & 31);
+        if (i < m) drow[mi] = dg[i];
+      }
+      // use the values here, so that their wait comes before the pass's
+      // loads are issued rather than behind them
+      asm volatile("" : "+v"(drow[0]), "+v"(drow[1]));
+    }
+    const u32x4_t rs = rsrc_words(xs, ubytes);
+    uint32_t base[NGC];
+    int cc[NGC];
+#pragma unroll
+    for (int q = 0; q < NGC; ++q) {
+      const int kr = 4 * (wave + NWV * q) + (lane >> 4);
+      const int col = 8 * ((lane & 15) ^ ((kr & 3) << 2));
+      cc[q] = col;
+      base[q] = kr < m ? static_cast<uint32_t>((static_cast<int64_t>(kr) * n + col) * 2) : kOOB;
+    }
+    auto issue = [&](char* sl, int c0) {
+      dma16_group<NGC>(
+          rs, static_cast<uint32_t>(c0 * 2), [&](int q) { return sl + (wave + NWV * q) * 1024; },
+          [&](int q) { return c0 + cc[q] < n ? base[q] : kOOB; });
+    };
+    an.zero();
+    if (dg != nullptr) {
+      column_pass_res(xd, f, next, an, drow, lo_in, lo_out, issue);
+      return;
+    }
+    issue(s0, 0);
+    issue(s1, SM);
+    issue(s2, 2 * SM);
+    for (int c = 0; c < nb; ++c) {
+      char* sl = (c % 3 == 0) ? s0 : ((c % 3 == 1) ? s1 : s2);
+      // wait for this wave's block-c loads; issued after them: blocks c + 1,
+      // c + 2 (8 loads each) and the stores of blocks c - 2, c - 1 (8 each)
+      if (c == 0)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC) : "memory");
+      else if (c == 1)
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC + NST) : "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC + 2 * NST) : "memory");
+      Acc ax;
+      block_product(sl, ax, false, drow);
+      {
         for_acc(wm, wn, lane, [&](int mi, int ni, int g, int i, int j) {
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) v[q] = f * ax.v[mi][ni][4 * g + q];
           *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
-        });
-      } else {
-        static_for<2>([&](auto MI) {
-          constexpr int mi = decltype(MI)::value;
-          u32x4_t lov[4], lon[4];
-#pragma unroll
-          for (int ch = 0; ch < 4; ++ch)
-            lov[ch] = lo_in ? __builtin_nontemporal_load(
-                                  reinterpret_cast<const u32x4_t*>(lo_chunk(lo_in, c, mi * 4 + ch)))
-                            : u32x4_t{0u, 0u, 0u, 0u};
-          static_for<2>([&](auto NI) {
-            static_for<4>([&](auto G) {
-              constexpr int ni = decltype(NI)::value, g = decltype(G)::value;
-              const int i = wm * 64 + mi * 32 + (lane & 31);
-              const int j = wn * 64 + ni * 32 + 8 * g + 4 * (lane >> 5);
-              const u32x4_t lc = lov[2 * ni + g / 2];
-              const uint32_t l0 = (g & 1) ? lc.z : lc.x, l1 = (g & 1) ? lc.w : lc.y;
-              const float lo[4] = {__uint_as_float(l0 << 16), __uint_as_float(l0 & 0xffff0000u),
-                                   __uint_as_float(l1 << 16), __uint_as_float(l1 & 0xffff0000u)};
-              float v[4], r[4];
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                v[q] = ax.v[mi][ni][4 * g + q];
-                if (lo_in) v[q] = muon::ns_lo_term(v[q], drow[mi], lo[q]);
-                v[q] = f * v[q];
-                r[q] = v[q] - muon::bf16_round(v[q]);
-              }
-              u32x4_t& lw = lon[2 * ni + g / 2];
-              if (g & 1) {
-                lw.z = muon::pack_bf16x2(r[0], r[1]);
-                lw.w = muon::pack_bf16x2(r[2], r[3]);
-              } else {
-                lw.x = muon::pack_bf16x2(r[0], r[1]);
-                lw.y = muon::pack_bf16x2(r[2], r[3]);
-              }
-              *reinterpret_cast<uint2*>(rt_at(am, i, j)) = pack4(v);
-            });
-          });
-          if (lo_out) {
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch)
-              __builtin_nontemporal_store(lon[ch], reinterpret_cast<u32x4_t*>(lo_chunk(lo_out, c, mi * 4 + ch)));
-          }
         });
       }
       barrier_lds();
