@@ -529,7 +529,8 @@ def main():
             achieved = fused_hbm / (t_dom * 1e-3) / 1e9
             breakdown["fused"]["gbs"] = round(achieved, 1)
             traffic = traffic_record(f"ns_small_kernel_traffic_{w.name}",
-                                     os.path.join(csrc, "ns_small.hip"), os.path.join(csrc, "ns_mfma_common.h"))
+                                     os.path.join(csrc, "ns_small.hip"), os.path.join(csrc, "ns_mfma_common.h"),
+                                     os.path.join(csrc, "muon_device.h"))
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                         "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                         "kernel": "ns_small_kernel (every iteration of units with m <= 128 in one launch)",
@@ -544,7 +545,8 @@ def main():
             if dom == "update":
                 traffic = traffic_record(f"update_kernel_traffic_{w.name}",
                                          os.path.join(csrc, "ns_gemm_mfma.hip"),
-                                         os.path.join(csrc, "ns_mfma_common.h"))
+                                         os.path.join(csrc, "ns_mfma_common.h"),
+                                         os.path.join(csrc, "muon_device.h"))
             what = {"update": "update X' = B' X, B' = a I + b A + c A A", "gram": "Gram A = X X^T",
                     "symsq": "B' = a I + b A + c A A", "prod": "m x m products of the Gram form"}[dom]
             roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
