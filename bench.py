@@ -521,14 +521,18 @@ def main():
             t = per_step[k][0]
             breakdown[k]["gbs"] = round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
             breakdown[k]["frac_hbm"] = round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if t > 0 else None
-        # the dominant Newton-Schulz kernel class by time
+        # the dominant Newton-Schulz kernel class by time; the HBM counter
+        # records were taken on the default iteration (5 fixed quintic steps,
+        # norms from the momentum pass, automatic fusion) and apply to it only
         dom = max(("gram", "symsq", "prod", "update", "fused"), key=lambda k: per_step[k][0])
+        default_ns = (args.ns_method == "quintic" and args.ns_coeffs == "fixed" and w.ns_steps == 5
+                      and args.norms == "momentum" and args.ns_fuse == "auto" and w.compute == "bf16")
         t_dom, n_dom = per_step[dom]
         csrc = os.path.join(ROOT, "newton_schulz_amd", "csrc")
         if dom == "fused" and t_dom > 0:
             achieved = fused_hbm / (t_dom * 1e-3) / 1e9
             breakdown["fused"]["gbs"] = round(achieved, 1)
-            traffic = traffic_record(f"ns_small_kernel_traffic_{w.name}",
+            traffic = None if not default_ns else traffic_record(f"ns_small_kernel_traffic_{w.name}",
                                      os.path.join(csrc, "ns_small.hip"), os.path.join(csrc, "ns_mfma_common.h"),
                                      os.path.join(csrc, "muon_device.h"))
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -542,7 +546,7 @@ def main():
         elif n_dom > 0 and t_dom > 0:
             achieved = ex[dom] / (t_dom * 1e-3) / 1e12
             traffic = None
-            if dom == "update":
+            if dom == "update" and default_ns:
                 traffic = traffic_record(f"update_kernel_traffic_{w.name}",
                                          os.path.join(csrc, "ns_gemm_mfma.hip"),
                                          os.path.join(csrc, "ns_mfma_common.h"),
