@@ -181,12 +181,13 @@ EXPERT_STATE_BYTES = 2 + 4 + 4              # bf16 gradient, fp32 momentum, fp32
 GIB = 1 << 30
 
 
-def expert_layers_that_fit(free_bytes: int, layers: int = 48) -> int:
+def expert_layers_that_fit(free_bytes: int, layers: int = 48, lanes: int = 1) -> int:
     """Largest layer count (<= layers) whose expert state fits in free device
-    memory with 4 GiB to spare beyond the step's own buffers (update buffer
-    and workspace, each bounded by the 1 GiB cap)."""
+    memory with 4 GiB to spare beyond the step's own buffers (per lane of
+    micro-buckets in flight: an update buffer and a workspace, each bounded by
+    the 1 GiB cap)."""
     per = EXPERT_LAYER_ELEMS * EXPERT_STATE_BYTES
-    return max(1, min(layers, (free_bytes - 4 * GIB - 2 * GIB) // per))
+    return max(1, min(layers, (free_bytes - 4 * GIB - 2 * GIB * lanes) // per))
 
 
 def step_times(run, steps: int):
@@ -387,7 +388,9 @@ def main():
                          "Newton-Schulz products of the workload's micro-buckets, as a yardstick")
     ap.add_argument("--offload", action="store_true",
                     help="momentum and gradient in host memory, copied per micro-bucket")
-    ap.add_argument("--inflight", type=int, default=2, help="--offload: micro-buckets on the device")
+    ap.add_argument("--inflight", type=int, default=None,
+                    help="micro-buckets in flight: lanes of the resident step (default 1), "
+                         "device slots with --offload (default 2)")
     ap.add_argument("--pageable", action="store_true", help="--offload: pageable host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip per-kernel event timing")
@@ -412,10 +415,15 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}), flush=True)
         return
+    if args.inflight is None:
+        args.inflight = 2 if args.offload else 1
+    if args.inflight < 1:
+        print("--inflight must be >= 1", file=sys.stderr)
+        sys.exit(2)
     layers_note = None
     if args.workload in ("qwen3_30b_experts:fit", "qwen3_30b_experts:48"):
         free = torch.cuda.mem_get_info(dev)[0]
-        L = expert_layers_that_fit(free)
+        L = expert_layers_that_fit(free, lanes=1 if args.offload else args.inflight)
         layers_note = {"layers_run": L, "layers_model": 48, "free_device_bytes": free,
                        "state_bytes_per_layer": EXPERT_LAYER_ELEMS * EXPERT_STATE_BYTES}
         args.workload = f"qwen3_30b_experts:{L}"
@@ -436,7 +444,8 @@ def main():
                   grad_dtype=w.grad_dtype, cap_bytes=w.cap_bytes, cap_kind=w.cap_kind,
                   ns_steps=w.ns_steps, keep_bf16_weights=keep_bf16, ns_method=args.ns_method,
                   ns_coeffs=None if args.ns_coeffs == "fixed" else args.ns_coeffs,
-                  norms_from_momentum=args.norms == "momentum", ns_fuse=args.ns_fuse)
+                  norms_from_momentum=args.norms == "momentum", ns_fuse=args.ns_fuse,
+                  inflight=args.inflight)
     g = torch.Generator(device=dev).manual_seed(w.seed)
     for i, W0 in enumerate(synth.iter_weights(w, g, dev)):
         ms.view(ms.master, i).copy_(W0)
@@ -454,15 +463,24 @@ def main():
     timing = not args.no_timing
     if timing:
         # one event pair per launch: size the pool from one step's launches
-        # (launches beyond the pool would go untimed)
-        ms.ctx.timing_enable(True, capacity=1 << 14)
-        ms.ctx.timing_reset()
+        # (launches beyond the pool would go untimed); one pool per lane
+        def timing_read():
+            tot = {}
+            for c in ms.contexts:
+                for k, (t, n) in c.timing_read().items():
+                    t0, n0 = tot.get(k, (0.0, 0))
+                    tot[k] = (t0 + t, n0 + n)
+            return tot
+        for c in ms.contexts:
+            c.timing_enable(True, capacity=1 << 14)
+            c.timing_reset()
         ms.step()
-        per = sum(v[1] for v in ms.ctx.timing_read().values())
-        ms.ctx.timing_enable(True, capacity=int(per * args.steps) + 64)
-        ms.ctx.timing_reset()
+        per = sum(v[1] for v in timing_read().values())
+        for c in ms.contexts:
+            c.timing_enable(True, capacity=int(per * args.steps) + 64)
+            c.timing_reset()
     ms_per_step, ms_median, ms_min, wall = step_times(ms.step, args.steps)
-    kt = ms.ctx.timing_read() if timing else {}
+    kt = timing_read() if timing else {}
 
     units = unit_list(w)
     fl = [ns_flops(m, n, w.ns_steps) for (m, n) in units]
@@ -558,6 +576,13 @@ def main():
                         "traffic": traffic, "kernel": f"ns_gemm_mfma_kernel ({what})",
                         "avg_launch_ms": round(t_dom / n_dom, 4),
                         "flop_per_launch_avg": int(ex[dom] / n_dom)}
+        if args.inflight > 1:
+            # lanes run concurrently: a launch's event interval includes time
+            # it shares the GPU with the other lanes' launches, so per-kernel
+            # rates understate the kernels and no roofline is claimed
+            roofline = None
+            breakdown["note"] = (f"{args.inflight} micro-buckets in flight: per-kernel event times "
+                                 "overlap across lanes and sum to more than the step")
 
     out = {
         "metric": METRIC if args.ns_method == "quintic" else METRIC.replace(
@@ -581,6 +606,7 @@ def main():
                    "ns_fuse": args.ns_fuse,
                    "micro_bucket_cap_bytes": w.cap_bytes, "cap_kind": w.cap_kind,
                    "micro_buckets": len(ms.plan.buckets), "workspace_bytes": ms.plan.max_workspace,
+                   "inflight_micro_buckets": args.inflight,
                    "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "ns_tflop_per_step_algorithmic": round(f_ns / 1e12, 4),

@@ -14,6 +14,18 @@ Newton-Schulz input/output buffer holds one micro-bucket, so device memory
 beyond the caller's state is cap-bounded: update buffer <= cap (full-byte
 caps), its partials (8 bytes per 4096 elements), plus the context workspace
 <= max over micro-buckets of the Newton-Schulz workspace.
+
+Micro-buckets in flight (the blog, section "Memory control" item 3: start
+with one bucket in flight, then try two): with inflight = k > 1 the step
+keeps k lanes, each with its own update buffer, partials and context
+workspace, and runs micro-bucket i on lane i % k: lane 0 on the caller's
+stream, the others on side streams of default priority that wait for the
+caller's stream at the start of the step and that it waits for at the end.
+Micro-buckets touch disjoint parts of the state, and each lane runs its
+micro-buckets in order, so the results are bit-identical for every k; what
+changes is that one lane's launches can fill the CUs another lane's leave
+idle (a launch's last, partial round of tiles, the epilogue bursts of short
+contractions).  Device memory beyond the state grows by (k - 1) lanes.
 """
 from __future__ import annotations
 
@@ -30,7 +42,11 @@ class MuonStep:
                  grad_dtype: torch.dtype = torch.bfloat16, cap_bytes: int = 512 << 20,
                  cap_kind: str = "full", ns_steps: int = 5, keep_bf16_weights: bool = False,
                  weight_decay: float = 0.0, scale: float = 1.0, ns_method: str = "quintic",
-                 ns_coeffs=None, norms_from_momentum: bool = True, ns_fuse: str = "auto"):
+                 ns_coeffs=None, norms_from_momentum: bool = True, ns_fuse: str = "auto",
+                 inflight: int = 1):
+        if inflight < 1:
+            raise ValueError("inflight must be >= 1")
+        self.inflight = inflight
         self.device = torch.device(device if device is not None else "cuda")
         if self.device.index is None:
             self.device = torch.device("cuda", torch.cuda.current_device())
@@ -62,10 +78,18 @@ class MuonStep:
         self.momentum = torch.zeros(off, dtype=torch.float32, device=dev)
         self.master = torch.zeros(off, dtype=torch.float32, device=dev)
         self.weight_bf16 = torch.zeros(off, dtype=torch.bfloat16, device=dev) if keep_bf16_weights else None
-        self.update = torch.empty(max(self.max_bucket, 1), dtype=self.cdtype, device=dev)
-        # per-4096-element sums of squares of the update, from the momentum pass
-        self.sq = torch.empty(max(sq_blocks(self.max_bucket), 1), dtype=torch.float64, device=dev)
-        self._work = self._bucket_work(self.update)
+        # per lane: context (workspace), update buffer, per-4096-element sums
+        # of squares of the update from the momentum pass, micro-bucket views
+        self.lanes: List[Tuple[Context, torch.Tensor, torch.Tensor, list]] = []
+        for k in range(self.inflight):
+            ctx = self.ctx if k == 0 else Context(dev, self.plan.max_workspace)
+            upd = torch.empty(max(self.max_bucket, 1), dtype=self.cdtype, device=dev)
+            sq = torch.empty(max(sq_blocks(self.max_bucket), 1), dtype=torch.float64, device=dev)
+            self.lanes.append((ctx, upd, sq, self._bucket_work(upd)))
+        _, self.update, self.sq, self._work = self.lanes[0]
+        self._side = [torch.cuda.Stream(dev) for _ in range(self.inflight - 1)]
+        self._ev_start = torch.cuda.Event()
+        self._ev_end = [torch.cuda.Event() for _ in self._side]
 
     def _bucket_work(self, update: torch.Tensor):
         """Per micro-bucket: its element range and its shape groups, each with
@@ -112,22 +136,41 @@ class MuonStep:
             self.ctx.momentum_update(self.grad[lo:hi], self.momentum[lo:hi], self.update[:hi - lo],
                                      self.beta, self.nesterov, stream)
 
-    def _run_bucket(self, grad, momentum, upd, sq, groups, want_sq, master, wb, stream, flag):
+    def _run_bucket(self, grad, momentum, upd, sq, groups, want_sq, master, wb, stream, flag, ctx=None):
         """momentum -> Newton-Schulz per shape group -> apply, for one
         micro-bucket whose update buffer `upd` is laid out as in _bucket_work."""
-        self.ctx.momentum_update(grad, momentum, upd, self.beta, self.nesterov, stream,
-                                 sq_partials=sq if want_sq else None)
-        self._run_nsa(upd, sq, groups, master, wb, stream, flag)
+        ctx = ctx if ctx is not None else self.ctx
+        ctx.momentum_update(grad, momentum, upd, self.beta, self.nesterov, stream,
+                            sq_partials=sq if want_sq else None)
+        self._run_nsa(upd, sq, groups, master, wb, stream, flag, ctx)
 
-    def _run_nsa(self, upd, sq, groups, master, wb, stream, flag):
+    def _run_nsa(self, upd, sq, groups, master, wb, stream, flag, ctx=None):
         """Newton-Schulz per shape group, in place on `upd`, then the apply."""
+        ctx = ctx if ctx is not None else self.ctx
         for h, mats, ptrs, whole in groups:
-            self.ctx.newton_schulz(mats, None, h, self.params, flag, stream, _ptrs=ptrs,
-                                   sq=(sq, upd) if whole else None)
-        self.ctx.apply(master, upd, self.lr, self.scale, self.weight_decay, wb, stream)
+            ctx.newton_schulz(mats, None, h, self.params, flag, stream, _ptrs=ptrs,
+                              sq=(sq, upd) if whole else None)
+        ctx.apply(master, upd, self.lr, self.scale, self.weight_decay, wb, stream)
+
+    @property
+    def contexts(self) -> List[Context]:
+        """The lanes' contexts (per-kernel timing is kept per context)."""
+        return [lane[0] for lane in self.lanes]
 
     def step(self, stream=None, nonfinite_flag: Optional[torch.Tensor] = None):
-        for lo, hi, groups, want_sq in self._work:
+        main = stream if stream is not None else torch.cuda.current_stream(self.device)
+        if self._side:
+            self._ev_start.record(main)
+            for sd in self._side:
+                sd.wait_event(self._ev_start)
+        for i in range(len(self._work)):
+            k = i % self.inflight
+            ctx, upd, sq, work = self.lanes[k]
+            lo, hi, groups, want_sq = work[i]
+            st = main if k == 0 else self._side[k - 1]
             wb = self.weight_bf16[lo:hi] if self.weight_bf16 is not None else None
-            self._run_bucket(self.grad[lo:hi], self.momentum[lo:hi], self.update[:hi - lo], self.sq,
-                             groups, want_sq, self.master[lo:hi], wb, stream, nonfinite_flag)
+            self._run_bucket(self.grad[lo:hi], self.momentum[lo:hi], upd[:hi - lo], sq, groups, want_sq,
+                             self.master[lo:hi], wb, st, nonfinite_flag, ctx)
+        for sd, ev in zip(self._side, self._ev_end):
+            ev.record(sd)
+            main.wait_event(ev)

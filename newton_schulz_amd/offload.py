@@ -118,10 +118,10 @@ class MuonOffloadStep(MuonStep):
                  timing: bool = False, **kw):
         if inflight < 1:
             raise ValueError("inflight must be >= 1")
-        self.inflight, self.pin = inflight, pin
+        self.pin = pin
         self.grads_on_host, self.update_to_host = grads_on_host, update_to_host
         self.timing = timing
-        super().__init__(shapes, device, **kw)
+        super().__init__(shapes, device, inflight=inflight, **kw)
 
     def _alloc_state(self, grad_dtype: torch.dtype, keep_bf16_weights: bool):
         n, dev = self.numel, self.device
@@ -143,6 +143,8 @@ class MuonOffloadStep(MuonStep):
                                     torch.empty(max(sq_blocks(mb), 1), dtype=torch.float64, device=dev),
                                     self._bucket_work(upd)))
         self.update, self.sq, self._work = self.slots[0].upd, self.slots[0].sq, self.slots[0].work
+        # one context: every Newton-Schulz call runs on the caller's stream
+        self.lanes = [(self.ctx, self.update, self.sq, self._work)]
         self.streams = {"h2d": torch.cuda.Stream(dev), "d2h": torch.cuda.Stream(dev)}
         self.schedule = offload_schedule(len(self.plan.buckets), self.inflight)
         # one event per (kind, slot), re-recorded for each micro-bucket that

@@ -129,3 +129,6 @@ def test_expert_layers_that_fit():
     assert bench.expert_layers_that_fit(10 ** 15) == 48
     assert bench.expert_layers_that_fit(45 * per + 6 * gib + per - 1) == 45
     assert bench.expert_layers_that_fit(0) == 1
+    # each further lane of micro-buckets in flight reserves 2 GiB more
+    assert bench.expert_layers_that_fit(48 * per + 6 * gib, lanes=2) == 47
+    assert bench.expert_layers_that_fit(48 * per + 8 * gib, lanes=2) == 48

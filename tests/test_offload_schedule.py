@@ -173,3 +173,12 @@ def test_checker_catches_planted_mistakes():
         check([early], 2)
     with pytest.raises(ValueError):
         offload_schedule(3, 0)
+
+
+def test_inflight_must_be_positive():
+    """Both steps reject zero micro-buckets in flight before touching a GPU."""
+    from newton_schulz_amd import MuonStep
+    from newton_schulz_amd.offload import MuonOffloadStep
+    for cls in (MuonStep, MuonOffloadStep):
+        with pytest.raises(ValueError, match="inflight"):
+            cls([(8, 8, 0)], "cuda:0", inflight=0)
