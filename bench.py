@@ -96,16 +96,20 @@ def fused_bytes(m: int, n: int, steps: int, gram: bool) -> int:
     return 2 * m * n * (1 + 2 * steps + 2 * max(0, steps - 2))
 
 
-def traffic_record(name: str, *kernel_src: str):
+def traffic_record(name: str, launches_per_step: float, *kernel_src: str):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
-    counter summary profiles/<name>.json, or None when missing or taken on
-    different kernel code (the kernel file and its local headers)."""
+    counter summary profiles/<name>.json, or None when missing, taken on
+    different kernel code (the kernel file and its local headers), or taken
+    when a step cut the work into a different number of launches (the record
+    covers one step: its dispatch count is the launches of that step)."""
     path = os.path.join(ROOT, "profiles", name + ".json")
     if not os.path.exists(path):
         return None
     from newton_schulz_amd.prof import source_fingerprint
     rec = json.load(open(path))
     if rec.get("source_code_sha256_16") != source_fingerprint(*kernel_src):
+        return None
+    if rec.get("dispatches") != round(launches_per_step):
         return None
     return round(rec.get("hbm_bytes_per_launch"))
 
@@ -550,7 +554,7 @@ def main():
         if dom == "fused" and t_dom > 0:
             achieved = fused_hbm / (t_dom * 1e-3) / 1e9
             breakdown["fused"]["gbs"] = round(achieved, 1)
-            traffic = None if not default_ns else traffic_record(f"ns_small_kernel_traffic_{w.name}",
+            traffic = None if not default_ns else traffic_record(f"ns_small_kernel_traffic_{w.name}", n_dom,
                                      os.path.join(csrc, "ns_small.hip"), os.path.join(csrc, "ns_mfma_common.h"),
                                      os.path.join(csrc, "muon_device.h"))
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
@@ -565,7 +569,7 @@ def main():
             achieved = ex[dom] / (t_dom * 1e-3) / 1e12
             traffic = None
             if dom == "update" and default_ns:
-                traffic = traffic_record(f"update_kernel_traffic_{w.name}",
+                traffic = traffic_record(f"update_kernel_traffic_{w.name}", n_dom,
                                          os.path.join(csrc, "ns_gemm_mfma.hip"),
                                          os.path.join(csrc, "ns_mfma_common.h"),
                                          os.path.join(csrc, "muon_device.h"))

@@ -92,30 +92,47 @@ class MuonStep:
         self._ev_end = [torch.cuda.Event() for _ in self._side]
 
     def _bucket_work(self, update: torch.Tensor):
-        """Per micro-bucket: its element range and its shape groups, each with
-        views of `update` (the micro-bucket laid out from its start) and the
-        cached pointer arrays of those views."""
+        """Per micro-bucket: its element range and its Newton-Schulz calls,
+        each with views of `update` (the micro-bucket laid out from its start)
+        and the cached pointer arrays of those views.
+
+        A per-head matrix (head_rows h < rows) is rows / h independent h x cols
+        units, each a contiguous block of the row-major matrix, so the calls
+        pass units rather than matrices: consecutive shape groups whose units
+        have one shape and follow each other in memory become one call (the
+        per-head q and k/v projections of a micro-bucket: one launch over all
+        their heads instead of one per shape, with one partial round of tiles
+        instead of one per call).  The units, and so the results, are the
+        same.  The merged call needs no more workspace than the separate ones
+        together, which the plan's per-micro-bucket figure already covers."""
         work = []
         pos = 0
         for b in self.plan.buckets:
             lo = b.elem_offset
             hi = lo + b.numel
-            groups = []
+            calls = []  # [unit rows, cols, unit offsets relative to lo]
             j = 0
             while j < len(b.indices):
                 k = j
                 while k < len(b.indices) and self.shapes[b.indices[k]] == self.shapes[b.indices[j]]:
                     k += 1
                 r, c, h = self.shapes[b.indices[j]]
-                rel = [self.offset[i] - lo for i in b.indices[j:k]]
-                mats = [update[o:o + r * c].view(r, c) for o in rel]
-                # norms from the momentum partials when every unit of the group
-                # starts on, and spans, whole 4096-element blocks
-                unit = (h if h else r) * c
-                whole = self.norms_from_momentum and unit % SQ_BLOCK == 0 and all(
-                    o % SQ_BLOCK == 0 for o in rel)
-                groups.append((h, mats, self.ctx.pointer_arrays(mats), whole))
+                ur = h if h else r
+                units = [self.offset[i] - lo + q * ur * c for i in b.indices[j:k] for q in range(r // ur)]
+                prev = calls[-1] if calls else None
+                if prev is not None and (prev[0], prev[1]) == (ur, c) and units[0] == prev[2][-1] + ur * c:
+                    prev[2].extend(units)
+                else:
+                    calls.append([ur, c, units])
                 j = k
+            groups = []
+            for ur, c, units in calls:
+                mats = [update[o:o + ur * c].view(ur, c) for o in units]
+                # norms from the momentum partials when every unit of the call
+                # starts on, and spans, whole 4096-element blocks
+                whole = self.norms_from_momentum and (ur * c) % SQ_BLOCK == 0 and all(
+                    o % SQ_BLOCK == 0 for o in units)
+                groups.append((0, mats, self.ctx.pointer_arrays(mats), whole))
             work.append((lo, hi, groups, any(g[3] for g in groups)))
             pos = hi
         assert pos == self.numel

@@ -6,6 +6,7 @@ m(m+1)n (Gram, upper triangle) + m^2(m+1) (symmetric square) + 2m^2 n
 (update); the dense-equivalent count is 2m^2 n + 2m^3 + 2m^2 n.  The totals
 below are those closed forms summed by hand over each workload's shapes.
 """
+import json
 import os
 import subprocess
 import sys
@@ -132,3 +133,21 @@ def test_expert_layers_that_fit():
     # each further lane of micro-buckets in flight reserves 2 GiB more
     assert bench.expert_layers_that_fit(48 * per + 6 * gib, lanes=2) == 47
     assert bench.expert_layers_that_fit(48 * per + 8 * gib, lanes=2) == 48
+
+
+def test_traffic_record_guards():
+    """A counter record is used only for the kernel code and the launches per
+    step it was taken on."""
+    csrc = os.path.join(bench.ROOT, "newton_schulz_amd", "csrc")
+    src = [os.path.join(csrc, f) for f in ("ns_gemm_mfma.hip", "ns_mfma_common.h", "muon_device.h")]
+    name = "update_kernel_traffic_qwen3_4b_36l"
+    rec = json.load(open(os.path.join(bench.ROOT, "profiles", name + ".json")))
+    n = rec["dispatches"]
+    assert bench.traffic_record(name, n + 1, *src) is None
+    assert bench.traffic_record(name, n / 2, *src) is None
+    assert bench.traffic_record("no_such_record", n, *src) is None
+    from newton_schulz_amd.prof import source_fingerprint
+    if rec["source_code_sha256_16"] == source_fingerprint(*src):
+        assert bench.traffic_record(name, n, *src) == round(rec["hbm_bytes_per_launch"])
+    else:
+        assert bench.traffic_record(name, n, *src) is None

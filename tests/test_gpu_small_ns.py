@@ -254,3 +254,51 @@ def test_fused_per_head_workload_sampled():
     say(f"  fused per-head workload: max rel err {worst:.3e}")
     assert worst <= BF16_TOL
     c.close()
+
+
+def test_step_merges_head_units_bit_identical():
+    """MuonStep passes the heads of a micro-bucket's per-head q and k/v
+    projections as one call of 128 x 2560 units (one fused launch instead of
+    one per shape); the update it applies equals per-matrix calls with
+    head_rows, bit for bit, momentum and apply included."""
+    from newton_schulz_amd import MuonStep
+    w = synth.qwen3_4b_heads(layers=6)
+    shapes = [(m.rows, m.cols, m.head_rows) for m in w.mats]
+    ms = MuonStep(shapes, DEV, lr=w.lr, beta=w.beta, nesterov=w.nesterov, cap_bytes=w.cap_bytes,
+                  keep_bf16_weights=True)
+    assert len(ms._work) == 1
+    _, _, groups, _ = ms._work[0]
+    assert len(groups) == 1 and groups[0][0] == 0 and len(groups[0][1]) == 6 * 48
+    g = gen(w.seed)
+    ms.grad.copy_(synth.normal((ms.numel,), w.grad_std, g, DEV, torch.bfloat16))
+    ms.master.copy_(synth.normal((ms.numel,), 0.02, g, DEV, torch.float32))
+    ms.momentum.copy_(synth.normal((ms.numel,), w.grad_std, g, DEV, torch.float32))
+    grad, mom, master = ms.grad.clone(), ms.momentum.clone(), ms.master.clone()
+    c = Context(DEV, ms.plan.max_workspace)
+    c.timing_enable(True, 64)
+    ms.ctx.timing_enable(True, 64)
+    ms.ctx.timing_reset()
+    ms.step()
+    # the same step by hand: one call per shape with head_rows
+    upd = torch.empty(ms.numel, dtype=torch.bfloat16, device=DEV)
+    sq = torch.empty(-(-ms.numel // 4096), dtype=torch.float64, device=DEV)
+    c.momentum_update(grad, mom, upd, w.beta, w.nesterov, sq_partials=sq)
+    by_shape = {}
+    for i, s in enumerate(shapes):
+        by_shape.setdefault(s, []).append(i)
+    c.timing_reset()
+    for (r, cl, h), idx in by_shape.items():
+        mats = [upd[ms.offset[i]:ms.offset[i] + r * cl].view(r, cl) for i in idx]
+        c.newton_schulz(mats, None, h, ns_params(), sq=(sq, upd))
+    wb = torch.empty(ms.numel, dtype=torch.bfloat16, device=DEV)
+    c.apply(master, upd, w.lr, 1.0, 0.0, wb)
+    torch.cuda.synchronize()
+    # 288 units in one call take the fused launch; 192 q and 96 k/v heads
+    # per call stay below one unit per CU and run as separate launches
+    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
+    assert ms.ctx.timing_read()["fused"][1] == (1 if 288 >= cus else 0)
+    assert c.timing_read()["fused"][1] == (len(by_shape) if 96 >= cus else 0)
+    assert torch.equal(ms.momentum, mom)
+    assert torch.equal(ms.master, master)
+    assert torch.equal(ms.weight_bf16, wb)
+    c.close()
