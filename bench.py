@@ -412,12 +412,24 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     if args.calibrate_copy:
+        # also a same-box reference for the streaming kernels: the median
+        # rate of the plain device copy (read + write bytes per second)
         src = torch.ones(args.calibrate_copy, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(3):
+        times = []
+        for i in range(3 + 10):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
             dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy}), flush=True)
+            b.record()
+            b.synchronize()
+            if i >= 3:
+                times.append(a.elapsed_time(b))
+        times.sort()
+        med = times[len(times) // 2]
+        print(json.dumps({"calibrate_copy_bytes": args.calibrate_copy, "copy_ms_median": round(med, 4),
+                          "copy_gbs_read_plus_write": round(2 * args.calibrate_copy / (med * 1e-3) / 1e9, 1)}),
+              flush=True)
         return
     if args.inflight is None:
         args.inflight = 2 if args.offload else 1
