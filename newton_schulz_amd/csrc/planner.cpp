@@ -111,6 +111,12 @@ static bool same_shape(const muon_shape_t& x, const muon_shape_t& y) {
   return x.rows == y.rows && x.cols == y.cols && x.head_rows == y.head_rows;
 }
 
+// a tall unit (more rows than columns) runs the other orientation of the
+// products (Y' = Y B'), in launches of its own
+static bool is_tall(const muon_shape_t& s) {
+  return (s.head_rows > 0 ? s.head_rows : s.rows) > s.cols;
+}
+
 extern "C" muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t count,
                                           size_t cap_bytes, int32_t cap_kind, int32_t compute,
                                           int32_t compute_units, muon_plan_t** out) {
@@ -144,13 +150,19 @@ extern "C" muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t co
       members[it->second].push_back(i);
     }
     for (size_t b = 0; b < keys.size(); ++b) {
-      // order members by exact shape, shapes in order of first appearance
+      // order members by orientation (that of the bucket's first member
+      // first), then by exact shape, shapes in order of first appearance:
+      // units of one orientation have one shape, and the members that give
+      // them lie together, so a caller can pass them as one call
       std::vector<muon_shape_t> order;
       for (int64_t i : members[b]) {
         bool seen = false;
         for (const auto& o : order) seen = seen || same_shape(o, shapes[i]);
         if (!seen) order.push_back(shapes[i]);
       }
+      const bool tall0 = is_tall(shapes[members[b][0]]);
+      std::stable_partition(order.begin(), order.end(),
+                            [&](const muon_shape_t& o) { return is_tall(o) == tall0; });
       std::vector<int64_t> sorted;
       for (const auto& o : order)
         for (int64_t i : members[b])
@@ -214,27 +226,33 @@ extern "C" muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t co
         // cut points minimising the time model: best[i] = cheapest plan of
         // the first i members, each micro-bucket a run within the cap (or a
         // single matrix)
+        // (a micro-bucket's two orientations are separate chains of
+        // launches, each with its own rounds of tiles)
         const size_t N = sorted.size();
         std::vector<size_t> c(N);
         std::vector<int64_t> u(N);
+        std::vector<char> tall(N);
         for (size_t i = 0; i < N; ++i) {
           const muon_shape_t& sh = shapes[sorted[i]];
           c[i] = cost(sorted[i]);
           u[i] = sh.head_rows > 0 ? sh.rows / sh.head_rows : 1;
+          tall[i] = is_tall(sh) ? 1 : 0;
         }
         std::vector<double> best(N + 1, 0.0);
         std::vector<size_t> from(N + 1, 0);
         for (size_t i = 1; i <= N; ++i) {
           best[i] = -1.0;
           size_t bytes = 0;
-          int64_t units = 0;
+          int64_t units[2] = {0, 0};
           for (size_t j = i; j-- > 0;) {
             bytes += c[j];
-            units += u[j];
+            units[tall[j]] += u[j];
             if (j + 1 < i && bytes > cap_bytes) break;
-            const double t = best[j] + kBucketOverhead +
-                             ns_time_model(keys[b].first, keys[b].second, units, compute_units,
-                                           compute);
+            double t = best[j];
+            for (int o = 0; o < 2; ++o)
+              if (units[o] > 0)
+                t += kBucketOverhead +
+                     ns_time_model(keys[b].first, keys[b].second, units[o], compute_units, compute);
             if (best[i] < 0.0 || t < best[i]) {
               best[i] = t;
               from[i] = j;

@@ -3,8 +3,9 @@
 State lives in flat device buffers laid out micro-bucket by micro-bucket
 (addresses planned once, views per step: the blog "Muon Optimizer + FSDP",
 sections "Memory control" item 2 and "DBuffer").  Per micro-bucket the step
-enqueues, on one stream and with no host synchronisation:
-    momentum (+ Nesterov) -> batched Newton-Schulz per shape group -> apply
+enqueues, on one stream (its lane's, below) and with no host
+synchronisation:
+    momentum (+ Nesterov) -> batched Newton-Schulz per unit shape -> apply
 (the blog's recommended chunked-execution pseudocode, minus the all-to-all
 exchanges, which one device does not need).  The momentum pass also leaves
 the sums of squares of every 4096-element block of the update, from which the

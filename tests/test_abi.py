@@ -342,3 +342,21 @@ def test_ns_params_coefficient_table():
         ns_params(steps=3, coeffs=[(1.0, 2.0, 3.0)])
     with pytest.raises(ValueError):
         ns_params(steps=3, coeffs="chebyshev")
+
+
+def test_plan_orientation_order_and_model():
+    """Inside a micro-bucket the members of the first member's orientation come
+    first (wide and tall units run as separate launch chains), and the
+    wave-aware cuts model each orientation's rounds on its own: the
+    Qwen3-4B (2560, 4096) bucket (36 tall q, 36 wide o) gets no micro-bucket
+    that mixes the two."""
+    shapes = [(2560, 4096, 0), (4096, 2560, 0), (2560, 4096, 0), (4096, 2560, 0)]
+    plan = Plan(shapes, 1 << 40, "full", "bf16")
+    assert len(plan.buckets) == 1 and plan.buckets[0].indices == [0, 2, 1, 3]
+    plan = Plan(_q4b_shapes(), 512 << 20, "full", "bf16", compute_units=256)
+    q4 = _q4b_shapes()
+    for b in plan.buckets:
+        tall = {q4[i][0] > q4[i][1] for i in b.indices}
+        assert len(tall) == 1, (b.m, b.n, b.indices)
+    sizes = sorted(b.count for b in plan.buckets if (b.m, b.n) == (2560, 4096))
+    assert sum(sizes) == 72
