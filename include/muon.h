@@ -229,7 +229,10 @@ typedef struct {
 /* Group `count` matrices into buckets by canonical unit shape (m, n) in order
  * of first appearance (blog section "Memory control", item 6: merge same-shape
  * matrices across layers into one bucket), order each bucket's members by
- * exact shape (stable), and cut each bucket into micro-buckets of whole
+ * orientation (units of the first member's orientation first: wide units,
+ * rows <= cols, and tall ones run separate launches) and then by exact shape
+ * (stable), so that members whose units share a shape lie together, and cut
+ * each bucket into micro-buckets of whole
  * matrices whose cost stays within `cap_bytes` (blog sections "Chunked
  * communication" and "Memory control", item 1: a separate Muon cap;
  * estimate_muon_peak(bucket) <= cap).  A matrix larger than the cap gets a
@@ -238,8 +241,9 @@ typedef struct {
  * compute_units = C > 0 (the device's CU count): the cut points are chosen,
  * still under the cap, to minimise a model of the Newton-Schulz time on C
  * CUs -- each product launch takes ceil(tiles / C) rounds of its per-tile
- * k-length -- plus a fixed cost per micro-bucket, so that launches do not end
- * with a nearly empty last round of tiles.  Host only; *out is owned by the
+ * k-length, each orientation of a micro-bucket its own launches -- plus a
+ * fixed cost per launch chain, so that launches do not end with a nearly
+ * empty last round of tiles.  Host only; *out is owned by the
  * caller (muon_plan_destroy).  Errors: MUON_EINVAL, MUON_ESHAPE. */
 muon_status_t muon_plan_create(const muon_shape_t* shapes, int64_t count, size_t cap_bytes,
                                int32_t cap_kind, int32_t compute, int32_t compute_units,
