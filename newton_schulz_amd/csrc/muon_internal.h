@@ -44,6 +44,13 @@ struct NsGemmArgs {
   float* dvec;
   const char* lo_in;
   char* lo_out;
+  // Only the units listed: ulist[0 .. *ucount) are unit indices in ascending
+  // order (the nonzero ones, launch_compact_units), and the tiles are those
+  // of the listed units, so a zero unit takes no tile slot; nullptr: every
+  // unit.  The residual plane is indexed by the listed tile number, so every
+  // product that reads or writes it must see the same list.
+  const int* ulist;
+  const int* ucount;
 };
 
 struct NsNormArgs {
@@ -90,6 +97,8 @@ hipError_t launch_apply(hipStream_t s, int cus, float* master, const void* upd, 
                         void* wbf, int64_t numel, float eta, float decay, int has_wd);
 
 hipError_t launch_norm(hipStream_t s, const NsNormArgs& a, int io_bf16, bool vec);
+// list[0 .. *count) = the units u < units with zflag[u] == 0, ascending.
+hipError_t launch_compact_units(hipStream_t s, const int* zflag, int64_t units, int* list, int* count);
 // out[u] = s[u] * in[u], element-wise over units of unit_elems (steps == 0, copies).
 hipError_t launch_scale_copy(hipStream_t s, MatRef in, MatRef out, int64_t unit_elems,
                              int64_t units, const float* scale, int io_bf16);

@@ -154,6 +154,31 @@ __global__ __launch_bounds__(256) void norm_from_blocks_kernel(NsNormArgs a) {
   if (threadIdx.x == 0) finish_unit(a, u, (ws[0] + ws[1]) + (ws[2] + ws[3]));
 }
 
+// The units whose norm is not zero, in ascending order, and their number:
+// one workgroup walks the flags 256 at a time; a wave's lanes count the
+// nonzero units before them with a ballot, the four wave counts give each
+// wave its offset, so every unit lands at its rank.
+__global__ __launch_bounds__(256) void compact_units_kernel(const int* __restrict__ zflag, int64_t units,
+                                                            int* __restrict__ list, int* __restrict__ count) {
+  __shared__ int wcnt[4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int64_t base = 0;  // nonzero units before this chunk
+  for (int64_t u0 = 0; u0 < units; u0 += 256) {
+    const int64_t u = u0 + threadIdx.x;
+    const bool keep = u < units && zflag[u] == 0;
+    const uint64_t mask = __ballot(keep);
+    const int before = __popcll(mask & ((uint64_t{1} << lane) - 1));
+    if (lane == 0) wcnt[wave] = __popcll(mask);
+    __syncthreads();
+    int off = 0;
+    for (int w = 0; w < wave; ++w) off += wcnt[w];
+    if (keep) list[base + off + before] = static_cast<int>(u);
+    base += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+    __syncthreads();  // wcnt is rewritten by the next chunk
+  }
+  if (threadIdx.x == 0) *count = static_cast<int>(base);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void scale_copy_kernel(MatRef in, MatRef out, int64_t n,
                                                          const float* scale) {
@@ -206,6 +231,12 @@ hipError_t launch_norm(hipStream_t s, const NsNormArgs& a, int io_bf16, bool vec
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_compact_units(hipStream_t s, const int* zflag, int64_t units, int* list, int* count) {
+  if (units <= 0 || units > 0x7fffffff) return hipErrorInvalidValue;
+  compact_units_kernel<<<1, 256, 0, s>>>(zflag, units, list, count);
+  return hipGetLastError();
 }
 
 hipError_t launch_scale_copy(hipStream_t s, MatRef in, MatRef out, int64_t unit_elems,

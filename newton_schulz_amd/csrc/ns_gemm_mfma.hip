@@ -198,7 +198,15 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   // the MALL (1-3% faster there); the symmetric square keeps one contiguous
   // run per XCD (the round-robin order measured 2% slower for it).  A
   // workgroup moves on to its next tile without leaving the CU.
-  const int64_t total = a.units * a.tiles_per_unit;
+  // With a unit list, only the listed units' tiles (a zero unit takes no
+  // slot, so the remaining tiles spread evenly over the workgroups); a list
+  // of every unit is not consulted.  List and count are read through the
+  // scalar cache (constant address space: nothing writes them during the
+  // launch), so a tile's unit costs no vector-memory round trip.
+  using cint_ptr = const __attribute__((address_space(4))) int*;
+  const int64_t nlisted = a.ulist != nullptr ? static_cast<int64_t>(*(cint_ptr)(a.ucount)) : a.units;
+  const bool use_list = nlisted != a.units;
+  const int64_t total = nlisted * a.tiles_per_unit;
   const int G = static_cast<int>(gridDim.x), hw = static_cast<int>(blockIdx.x);
   const int xg = hw % 8, q8 = G / 8, r8 = G % 8;
   const int cnt = q8 + (xg < r8 ? 1 : 0);
@@ -212,6 +220,7 @@ __global__ __launch_bounds__(128 * NWN, 1) void ns_gemm_mfma_kernel(NsGemmArgs a
   auto coords = [&](int64_t l, int64_t& uu, int& ti, int& tj) __attribute__((always_inline)) {
     uu = l / a.tiles_per_unit;
     const int t = static_cast<int>(l - uu * a.tiles_per_unit);
+    if (use_list) uu = ((cint_ptr)(a.ulist))[uu];
     if (EPI == EPI_UPDATE) {
       // grouped raster: bands of up to GN tile columns, row-major inside a
       // band, so the ~32 tiles an XCD runs at once form an 8 x 4 block that
