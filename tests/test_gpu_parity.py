@@ -209,6 +209,38 @@ def test_ns_zero_units_exact(ctx):
     assert not torch.any(zo[0])
 
 
+@pytest.mark.parametrize("shape", [(768, 2048), (2048, 768), (256, 512)])
+def test_ns_zero_units_take_no_slot(ctx, shape):
+    """The updates run over a device-built list of the nonzero units: with
+    zero units interleaved (and an all-zero call) every nonzero unit equals,
+    bit for bit, the same unit in a call without the zero ones, and the zero
+    units come out exactly zero."""
+    g = gen(12)
+    zero = {0, 3, 4, 9, 11}
+    mats = [synth.normal(shape, 1e-3, g, DEV, torch.bfloat16) for _ in range(12)]
+    for i in zero:
+        mats[i].zero_()
+    out = [torch.full_like(m, 5.0) for m in mats]
+    ctx.newton_schulz(mats, out)
+    dense = [m for i, m in enumerate(mats) if i not in zero]
+    dout = [torch.empty_like(m) for m in dense]
+    ctx.newton_schulz(dense, dout)
+    allz = [torch.zeros_like(mats[0]) for _ in range(3)]
+    zout = [torch.full_like(m, 5.0) for m in allz]
+    ctx.newton_schulz(allz, zout)
+    torch.cuda.synchronize()
+    k = 0
+    for i in range(12):
+        if i in zero:
+            assert not torch.any(out[i]), i
+        else:
+            assert torch.equal(out[i], dout[k]), i
+            k += 1
+    assert all(not torch.any(z) for z in zout)
+    ref = oracle.ns_ref(host(mats[1]))
+    assert oracle.rel_fro(host(out[1]), ref) <= BF16_TOL
+
+
 def test_ns_nonfinite_flag(ctx):
     g = gen(4)
     mats = [synth.normal((128, 256), 1e-3, g, DEV, torch.bfloat16) for _ in range(2)]
