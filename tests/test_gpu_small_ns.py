@@ -9,7 +9,6 @@ per-class launch counts.
 """
 import sys
 
-import numpy as np
 import pytest
 import torch
 
