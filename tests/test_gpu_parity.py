@@ -6,6 +6,7 @@ fp32 mode; zero units exactly zero; identical inputs give identical bits.
 Inputs are seeded synthetic draws (newton_schulz_amd.synth); the oracle gets
 exact host copies of the device inputs.
 """
+import os
 import sys
 
 import numpy as np
@@ -378,10 +379,13 @@ def test_qwen3_4b_full_model_sampled():
         fill_grads(ms, w, g)
         ms.momentum_only()
     fill_grads(ms, w, g)
-    # the first and last matrix of every micro-bucket, plus 8 seeded picks
+    # the first and last matrix of every micro-bucket, plus 8 seeded picks;
+    # MUON_PARITY_FULL=1: all 252 matrices (some minutes of fp64 on the host)
     rng = np.random.default_rng(2)
     picks = {b.indices[0] for b in ms.plan.buckets} | {b.indices[-1] for b in ms.plan.buckets}
     picks |= {int(x) for x in rng.choice(len(w.mats), 8, replace=False)}
+    if os.environ.get("MUON_PARITY_FULL") == "1":
+        picks = set(range(len(w.mats)))
     picks = sorted(picks)
     say(f"  qwen3_4b: {len(ms.plan.buckets)} micro-buckets, {len(picks)} matrices checked")
     G = {i: host(ms.view(ms.grad, i)) for i in picks}
