@@ -2,9 +2,10 @@
 // launch (bf16 MFMA, fp32 accumulation), e.g. the per-head 128 x 2560 q/k/v
 // matrices of per-head Muon.
 //
-// One workgroup owns one unit for all iterations: 4 waves, 2 x 2 over a
-// 128 x 128 output, 64 x 64 each (the layout of the 128 x 128 tiles of the
-// separate product launches).  A and B' stay in LDS as bf16; the m x n
+// One workgroup owns one unit for all iterations: 8 waves, 2 x 4 over a
+// 128 x 128 output, 64 x 32 each; every 32 x 32 accumulator takes the
+// operands of the 128 x 128 tiles of the separate product launches in their
+// order.  A and B' stay in LDS as bf16; the m x n
 // iterate streams through LDS in 128-column blocks.  With X_0 = s Y
 // (s = 1 / (||Y||_F + eps)) folded into the first products:
 //   A_0 = s^2 Y Y^T                          one pass over the input
@@ -27,7 +28,9 @@
 namespace {
 
 constexpr int SM = 128;            // rows and columns of A and B' (m padded)
-constexpr int NWV = 4;             // waves
+constexpr int NWV = 8;             // waves: 2 along the rows x NWV / 2 along the columns
+constexpr int WNC = SM / (NWV / 2);   // output columns per wave
+constexpr int FN = WNC / 32;          // 32-column accumulator blocks per wave
 constexpr int HALF = SM * 64 * 2;  // one 64-k half of a 128-row K-contiguous tile
 constexpr int SLAB = SM * SM * 2;  // a 128 x 128 bf16 block
 constexpr int NGR = SM / (8 * NWV);   // row-slab DMA instructions per wave (128 rows x 64 k)
@@ -59,32 +62,32 @@ __device__ __forceinline__ bf16x8_t kt_frag(const char* t, int rb, int kk, int l
 }
 
 struct Acc {
-  f32x16_t v[2][2];
+  f32x16_t v[2][FN];
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) v[mi][ni] = (f32x16_t)(0.0f);
+      for (int ni = 0; ni < FN; ++ni) v[mi][ni] = (f32x16_t)(0.0f);
   }
   // acc += P_M P_N^T over one k16 step; fa: N side, fb: M side
-  __device__ __forceinline__ void mma(const bf16x8_t (&fa)[2], const bf16x8_t (&fb)[2]) {
+  __device__ __forceinline__ void mma(const bf16x8_t (&fa)[FN], const bf16x8_t (&fb)[2]) {
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
+      for (int ni = 0; ni < FN; ++ni)
         v[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ni], fb[mi], v[mi][ni], 0, 0, 0);
   }
 };
 
 // Lane l holds row wm 64 + mi 32 + l % 32 and, per register group g, columns
-// wn 64 + ni 32 + 8 g + 4 (l / 32) + 0..3 of the accumulated product.
+// wn WNC + ni 32 + 8 g + 4 (l / 32) + 0..3 of the accumulated product.
 template <typename F>
 __device__ __forceinline__ void for_acc(int wm, int wn, int lane, F&& f) {
   static_for<2>([&](auto MI) {
-    static_for<2>([&](auto NI) {
+    static_for<FN>([&](auto NI) {
       static_for<4>([&](auto G) {
         constexpr int mi = decltype(MI)::value, ni = decltype(NI)::value, g = decltype(G)::value;
-        f(mi, ni, g, wm * 64 + mi * 32 + (lane & 31), wn * 64 + ni * 32 + 8 * g + 4 * (lane >> 5));
+        f(mi, ni, g, wm * 64 + mi * 32 + (lane & 31), wn * WNC + ni * 32 + 8 * g + 4 * (lane >> 5));
       });
     });
   });
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / (NWV / 2), wn = wave % (NWV / 2);
   const int64_t u = blockIdx.x;
   const int m = a.m, n = a.n;
   const uint32_t ubytes = static_cast<uint32_t>(static_cast<int64_t>(m) * n * 2);
@@ -179,12 +182,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(NGR) : "memory");
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        bf16x8_t fa[2], fb[2];
+        bf16x8_t fa[FN], fb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          fa[i] = rt_frag(st, wn * 64 + i * 32, kk, lane);
-          fb[i] = rt_frag(st, wm * 64 + i * 32, kk, lane);
-        }
+        for (int i = 0; i < FN; ++i) fa[i] = rt_frag(st, wn * WNC + i * 32, kk, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fb[i] = rt_frag(st, wm * 64 + i * 32, kk, lane);
         acc.mma(fa, fb);
       }
       barrier_lds();  // every wave is done with stage kt's buffer
@@ -208,12 +210,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     acc.zero();
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      bf16x8_t fa[2], fb[2];
+      bf16x8_t fa[FN], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fa[i] = rt_frag(yy, wn * 64 + i * 32, kk, lane);
-        fb[i] = rt_frag(x, wm * 64 + i * 32, kk, lane);
-      }
+      for (int i = 0; i < FN; ++i) fa[i] = rt_frag(yy, wn * WNC + i * 32, kk, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fb[i] = rt_frag(x, wm * 64 + i * 32, kk, lane);
       acc.mma(fa, fb);
     }
   };
@@ -266,12 +267,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       ax.zero();
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        bf16x8_t fa[2], fb[2];
+        bf16x8_t fa[FN], fb[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          fa[i] = kt_frag(sl, wn * 64 + i * 32, kk, lane);
-          fb[i] = rt_frag(bp, wm * 64 + i * 32, kk, lane);
-        }
+        for (int i = 0; i < FN; ++i) fa[i] = kt_frag(sl, wn * WNC + i * 32, kk, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) fb[i] = rt_frag(bp, wm * 64 + i * 32, kk, lane);
         ax.mma(fa, fb);
         if (diag && (kk >> 2) == wm) {
           const int mis = (kk >> 1) & 1;
@@ -284,13 +284,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
           const int q = e >> 1;
           const u32x4_t v = {q == 0 ? w : 0u, q == 1 ? w : 0u, q == 2 ? w : 0u, q == 3 ? w : 0u};
           const bf16x8_t fd = __builtin_bit_cast(bf16x8_t, v);
-          if (mis == 0) {
-            ax.v[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fd, ax.v[0][0], 0, 0, 0);
-            ax.v[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fd, ax.v[0][1], 0, 0, 0);
-          } else {
-            ax.v[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fd, ax.v[1][0], 0, 0, 0);
-            ax.v[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fd, ax.v[1][1], 0, 0, 0);
-          }
+          static_for<FN>([&](auto NI) {
+            constexpr int ni = decltype(NI)::value;
+            if (mis == 0)
+              ax.v[0][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ni], fd, ax.v[0][ni], 0, 0, 0);
+            else
+              ax.v[1][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ni], fd, ax.v[1][ni], 0, 0, 0);
+          });
         }
       }
   };
@@ -307,19 +307,20 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
   // order) -- the wait counts below.
   auto column_pass_res = [&](const bf16_t* xd, float f, bool next, Acc& an, const float (&drow)[2],
                              const char* lo_in, char* lo_out, auto&& issue_x) {
+    // memory operations per wave: NGC per iterate block, NLO per residual
+    // block, NST X' stores and NLS residual stores per block
+    constexpr int NLO = 4 * FN, NLS = 4 * FN;
+    static_assert(NGC == 4 && NST == 4 && NLO == 4 && NLS == 4,
+                  "wait counts below assume 4 operations per group");
     const u32x4_t lrs = rsrc_words(lo_in ? lo_in : lo_out, static_cast<uint32_t>(nb) * SLAB);
     auto issue_lo = [&](char* buf, int c) {
       if (lo_in == nullptr) return;
-      dma16_group<8>(
+      dma16_group<NLO>(
           lrs, static_cast<uint32_t>(c) * SLAB, [&](int q) { return buf + (wave + NWV * q) * 1024; },
           [&](int q) { return c < nb ? static_cast<uint32_t>((wave + NWV * q) * 1024 + lane * 16) : kOOB; });
     };
     auto slab = [&](int c) { return (c & 1) ? s1 : s0; };
     auto lobuf = [&](int c) { return (c & 1) ? am : s2; };
-    // memory operations per wave: NGC per iterate block, 8 per residual
-    // block, NST X' stores and 8 residual stores per block
-    constexpr int NLO = 8, NLS = 8;
-    static_assert(NGC == 8 && NST == 8, "wait counts below assume 8 operations per group");
     const int n_in = (lo_in ? NLO : 0) + NGC;
     const int n_out = (lo_out ? NLS : 0) + NST;
     issue_lo(lobuf(0), 0);
@@ -328,33 +329,33 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     issue_x(slab(1), SM);
     for (int c = 0; c < nb; ++c) {
       char* sl = slab(c);
-      const int nw = (c == 0 ? 0 : n_out) + n_in;  // 8 .. 32, a multiple of 8
-      if (nw == 8)
+      const int nw = (c == 0 ? 0 : n_out) + n_in;  // 4 .. 16, a multiple of 4
+      if (nw == 4)
+        asm volatile("s_waitcnt vmcnt(4)\n\ts_barrier" ::: "memory");
+      else if (nw == 8)
         asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-      else if (nw == 16)
-        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-      else if (nw == 24)
-        asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+      else if (nw == 12)
+        asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
       else
-        asm volatile("s_waitcnt vmcnt(32)\n\ts_barrier" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
       Acc ax;
       block_product(sl, ax, true, drow);
       // this wave's residual chunks of block c, from the pieces it fetched
-      u32x4_t lov[8];
+      u32x4_t lov[NLO];
 #pragma unroll
-      for (int ch = 0; ch < 8; ++ch)
+      for (int ch = 0; ch < NLO; ++ch)
         lov[ch] = lo_in ? *reinterpret_cast<const u32x4_t*>(lobuf(c) + (ch * NWV + wave) * 1024 + lane * 16)
                         : u32x4_t{0u, 0u, 0u, 0u};
       barrier_lds();  // every wave is done reading block c: stage X' over it
       static_for<2>([&](auto MI) {
         constexpr int mi = decltype(MI)::value;
-        u32x4_t lon[4];
-        static_for<2>([&](auto NI) {
+        u32x4_t lon[2 * FN];
+        static_for<FN>([&](auto NI) {
           static_for<4>([&](auto G) {
             constexpr int ni = decltype(NI)::value, g = decltype(G)::value;
             const int i = wm * 64 + mi * 32 + (lane & 31);
-            const int j = wn * 64 + ni * 32 + 8 * g + 4 * (lane >> 5);
-            const u32x4_t lc = lov[mi * 4 + 2 * ni + g / 2];
+            const int j = wn * WNC + ni * 32 + 8 * g + 4 * (lane >> 5);
+            const u32x4_t lc = lov[mi * 2 * FN + 2 * ni + g / 2];
             const uint32_t l0 = (g & 1) ? lc.z : lc.x, l1 = (g & 1) ? lc.w : lc.y;
             const float lo[4] = {__uint_as_float(l0 << 16), __uint_as_float(l0 & 0xffff0000u),
                                  __uint_as_float(l1 << 16), __uint_as_float(l1 & 0xffff0000u)};
@@ -379,10 +380,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
         });
         if (lo_out) {
 #pragma unroll
-          for (int ch = 0; ch < 4; ++ch)
+          for (int ch = 0; ch < 2 * FN; ++ch)
             __builtin_nontemporal_store(
                 lon[ch], reinterpret_cast<u32x4_t*>(lo_out + static_cast<int64_t>(c) * SLAB +
-                                                    ((mi * 4 + ch) * NWV + wave) * 1024 + lane * 16));
+                                                    ((mi * 2 * FN + ch) * NWV + wave) * 1024 + lane * 16));
         }
       });
       barrier_lds();
@@ -390,12 +391,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       if (next) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-          bf16x8_t fa[2], fb[2];
+          bf16x8_t fa[FN], fb[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            fa[i] = rt_frag(sl, wn * 64 + i * 32, kk, lane);
-            fb[i] = rt_frag(sl, wm * 64 + i * 32, kk, lane);
-          }
+          for (int i = 0; i < FN; ++i) fa[i] = rt_frag(sl, wn * WNC + i * 32, kk, lane);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) fb[i] = rt_frag(sl, wm * 64 + i * 32, kk, lane);
           an.mma(fa, fb);
         }
       }
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
   // diagonal is completed and the iterate's residual carried
   // (ns_diag_residual, ns_lo_term) in column_pass_res: lo_in / lo_out are the
   // unit's residual planes (one 32 KiB block per column block, each lane's
-  // values of a 32-row block as four contiguous 16-byte chunks; lo_in null
+  // values of a 32-row block as 2 FN contiguous 16-byte chunks; lo_in null
   // for the exact bf16 input, lo_out null when not kept).  Without dg, three
   // iterate blocks rotate through s0 .. s2 and X' is staged in am.
   auto column_pass = [&](const bf16_t* xs, const bf16_t* xd, float f, bool next, Acc& an,
@@ -454,7 +454,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
     for (int c = 0; c < nb; ++c) {
       char* sl = (c % 3 == 0) ? s0 : ((c % 3 == 1) ? s1 : s2);
       // wait for this wave's block-c loads; issued after them: blocks c + 1,
-      // c + 2 (8 loads each) and the stores of blocks c - 2, c - 1 (8 each)
+      // c + 2 (NGC loads each) and the stores of blocks c - 2, c - 1 (NST each)
       if (c == 0)
         asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(2 * NGC) : "memory");
       else if (c == 1)
@@ -476,12 +476,11 @@ __global__ __launch_bounds__(64 * NWV, 1) void ns_small_kernel(NsSmallArgs a) {
       if (next) {
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk) {
-          bf16x8_t fa[2], fb[2];
+          bf16x8_t fa[FN], fb[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            fa[i] = rt_frag(am, wn * 64 + i * 32, kk, lane);
-            fb[i] = rt_frag(am, wm * 64 + i * 32, kk, lane);
-          }
+          for (int i = 0; i < FN; ++i) fa[i] = rt_frag(am, wn * WNC + i * 32, kk, lane);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) fb[i] = rt_frag(am, wm * 64 + i * 32, kk, lane);
           an.mma(fa, fb);
         }
       }
