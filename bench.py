@@ -196,7 +196,7 @@ def expert_layers_that_fit(free_bytes: int, layers: int = 48, lanes: int = 1) ->
 
 def step_times(run, steps: int):
     """Run `steps` steps between HIP events on the current stream: mean, median
-    and min ms per step, and the host wall time."""
+    and min ms per step, the host wall time and every step's ms."""
     import statistics
     import torch
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -209,7 +209,7 @@ def step_times(run, steps: int):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
-    return ev[0].elapsed_time(ev[-1]) / steps, statistics.median(per), min(per), wall
+    return ev[0].elapsed_time(ev[-1]) / steps, statistics.median(per), min(per), wall, per
 
 
 def host_cores():
@@ -282,7 +282,7 @@ def run_library_gemm(args, w, dev):
                                 ("gram", lambda: torch.bmm(X, Xt), 2 * m * m * n * U)):
             for _ in range(3):
                 fn()
-            mean, med, mn, _ = step_times(fn, max(args.steps, 5))
+            mean, med, mn, _, _ = step_times(fn, max(args.steps, 5))
             res[name] = {"ms_median": round(med, 4), "tflops_median": round(flops / (med * 1e-3) / 1e12, 1),
                          "tflops_best": round(flops / (mn * 1e-3) / 1e12, 1)}
         rows.append(res)
@@ -316,7 +316,7 @@ def run_offload(args, w, dev):
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         off.step()
-    mean, med, mn, wall = step_times(off.step, args.steps)
+    mean, med, mn, wall, per = step_times(off.step, args.steps)
     # one more step with events around every copy and compute stage
     off.timing = True
     off.step()
@@ -341,6 +341,7 @@ def run_offload(args, w, dev):
         "ms_per_step": round(mean, 3),
         "ms_per_step_median": round(med, 3),
         "ms_per_step_min": round(mn, 3),
+        "ms_steps": [round(t, 2) for t in per],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
@@ -495,7 +496,7 @@ def main():
         for c in ms.contexts:
             c.timing_enable(True, capacity=int(per * args.steps) + 64)
             c.timing_reset()
-    ms_per_step, ms_median, ms_min, wall = step_times(ms.step, args.steps)
+    ms_per_step, ms_median, ms_min, wall, per = step_times(ms.step, args.steps)
     kt = timing_read() if timing else {}
 
     units = unit_list(w)
@@ -611,6 +612,7 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "ms_per_step_median": round(ms_median, 4),
         "ms_per_step_min": round(ms_min, 4),
+        "ms_per_step_max": round(max(per), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
