@@ -139,9 +139,6 @@ class MuonStep:
         assert pos == self.numel
         return work
 
-    def _uview(self, off: int, r: int, c: int) -> torch.Tensor:
-        return self.update[off:off + r * c].view(r, c)
-
     def view(self, buf: torch.Tensor, i: int) -> torch.Tensor:
         """Matrix i of a flat state buffer (grad, momentum, master, weight_bf16)."""
         r, c, _ = self.shapes[i]
