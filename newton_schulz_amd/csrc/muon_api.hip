@@ -540,8 +540,9 @@ muon_status_t ns_batched(const NsEnv& env, void* stream, const void* const* mats
     return e == hipSuccess ? MUON_OK : ehip(env, e, "copy launch");
   }
   auto gemm = [&](int cls, NsGemmArgs& a, int epi, bool tm, bool tn) -> hipError_t {
-    // 256 x 256 tiles once the smaller output side reaches 256
-    const int T = mfma ? ((std::min(a.M, a.N) >= 256) ? 256 : 128) : 64;
+    // 256 x 256 tiles once the smaller output side reaches 256, 128 x 128
+    // where that leaves most CUs idle (the same bits either way)
+    const int T = mfma ? ns_mfma_tile(a.M, a.N, epi != EPI_UPDATE, L.units, env.cus) : 64;
     setup(a, epi, T);
     const long k = etstart(env, s, cls);
     const hipError_t r = mfma ? launch_ns_gemm_mfma(s, a, epi, tm, tn, T)

@@ -13,8 +13,9 @@
 //   zflag    int per unit                   ||Y||_F == 0
 //   partial  double per unit and part       norm partial sums
 //   lo       bf16 residual plane per unit   the iterate's part below bf16
-//            (BF16 compute only; tile-padded: the products' tiles of T x T,
-//            T = 256 once m >= 256, else 128)
+//            (BF16 compute only; padded to whole 256 x 256 tiles once
+//            m >= 256, else 128 x 128, which also holds the 128-tiles that
+//            ns_mfma_tile may pick for m >= 256)
 //   dvec     float per unit and row of A    diagonal of B' before rounding
 struct NsLayout {
   int64_t units = 0, ur = 0, uc = 0, m = 0, n = 0;
@@ -25,3 +26,11 @@ struct NsLayout {
 };
 
 bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* L);
+
+// Output tile side of one bf16 MFMA product launch over `units` outputs of
+// rows x cols (upper-triangle tiles only when `upper`): 256 once the smaller
+// side reaches 256, else 128 -- and 128 also where the launch has so few
+// 256-tiles that 128-tiles, two workgroups per CU, finish sooner.  Every
+// accumulator sums the same products in the same order at either size, so
+// the choice changes the time, not the result.
+int ns_mfma_tile(int64_t rows, int64_t cols, bool upper, int64_t units, int cus);

@@ -22,20 +22,32 @@ inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// A round of 128-tiles (two workgroups of four waves per CU) takes about
+// this fraction of the time of a round of 256-tiles at the same K (MI355X:
+// 0.58 for the update and 0.49 for the symmetric square at K = 768, many
+// rounds each); the margin keeps 256-tiles wherever the two are close.
+constexpr double kRound128 = 0.6;
+
 // Model of the Newton-Schulz time of one micro-bucket of U units of
 // canonical shape (m, n) on `cus` compute units, in k-elements processed per
-// tile slot: every product launch takes ceil(tiles / slots) rounds, a round
-// as long as its contraction (Gram: n, symmetric square and update: m).
-// Tile side and slots per CU follow the kernels: 256 x 256 (one per CU) once
-// m >= 256 in bf16, else 128 x 128 (two per CU); fp32 runs 64 x 64 tiles.
+// 256-tile slot: every product launch takes ceil(tiles / slots) rounds, a
+// round as long as its contraction (Gram: n, symmetric square and update:
+// m), a round of 128-tiles kRound128 of that.  Tile side and slots per CU
+// follow the launches: bf16 products take ns_mfma_tile's side (one 256-tile
+// or two 128-tiles per CU), fp32 runs 64 x 64 tiles (four per CU).
+
 double ns_time_model(int64_t m, int64_t n, int64_t units, int cus, int32_t compute) {
-  const int64_t tile = compute == MUON_F32 ? 64 : (m >= 256 ? 256 : 128);
-  const int64_t slots = static_cast<int64_t>(cus) * (tile == 256 ? 1 : (tile == 128 ? 2 : 4));
-  const int64_t tm = ceil_div(m, tile), tn = ceil_div(n, tile);
-  const int64_t rounds_sym = ceil_div(units * (tm * (tm + 1) / 2), slots);
-  const int64_t rounds_upd = ceil_div(units * tm * tn, slots);
-  return static_cast<double>(rounds_sym) * static_cast<double>(n + m) +
-         static_cast<double>(rounds_upd) * static_cast<double>(m);
+  // rounds of tiles of one launch, a round of 128-tiles weighted kRound128
+  auto rounds = [&](int64_t rows, int64_t cols, bool upper) -> double {
+    const int64_t tile = compute == MUON_F32 ? 64 : ns_mfma_tile(rows, cols, upper, units, cus);
+    const int64_t slots = static_cast<int64_t>(cus) * (tile == 256 ? 1 : (tile == 128 ? 2 : 4));
+    const int64_t tm = ceil_div(rows, tile), tn = ceil_div(cols, tile);
+    const int64_t r = ceil_div(units * (upper ? tm * (tm + 1) / 2 : tm * tn), slots);
+    return static_cast<double>(r) * (tile == 128 ? kRound128 : 1.0);
+  };
+  // Gram (K = n) and symmetric square (K = m) over the m x m upper tiles,
+  // update (K = m) over the m x n tiles
+  return rounds(m, m, true) * static_cast<double>(n + m) + rounds(m, n, false) * static_cast<double>(m);
 }
 
 // Fixed cost of one more micro-bucket in the same units: about 20 dependent
@@ -44,6 +56,17 @@ double ns_time_model(int64_t m, int64_t n, int64_t units, int cus, int32_t compu
 constexpr double kBucketOverhead = 3000.0;
 
 }  // namespace
+
+int ns_mfma_tile(int64_t rows, int64_t cols, bool upper, int64_t units, int cus) {
+  if (std::min(rows, cols) < 256) return 128;
+  const int64_t c = cus > 0 ? cus : 256;
+  auto tiles = [&](int64_t t) {
+    const int64_t tm = ceil_div(rows, t), tn = ceil_div(cols, t);
+    return units * (upper ? tm * (tm + 1) / 2 : tm * tn);
+  };
+  const int64_t r256 = ceil_div(tiles(256), c), r128 = ceil_div(tiles(128), 2 * c);
+  return kRound128 * static_cast<double>(r128) < static_cast<double>(r256) ? 128 : 256;
+}
 
 // Shared with muon_api.hip, so the reported size and the carve-up agree.
 bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* L) {
