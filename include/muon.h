@@ -240,8 +240,11 @@ typedef struct {
  * compute_units = 0: micro-buckets are filled greedily up to the cap.
  * compute_units = C > 0 (the device's CU count): the cut points are chosen,
  * still under the cap, to minimise a model of the Newton-Schulz time on C
- * CUs -- each product launch takes ceil(tiles / C) rounds of its per-tile
- * k-length, each orientation of a micro-bucket its own launches -- plus a
+ * CUs -- each product launch takes ceil(tiles / slots) rounds of its
+ * per-tile k-length (one 256-tile per CU, or two 128-tiles per CU at 0.6 of
+ * a 256-tile round where the launch takes those because few 256-tiles would
+ * leave most CUs idle), each orientation of a micro-bucket its own
+ * launches -- plus a
  * fixed cost per launch chain, so that launches do not end with a nearly
  * empty last round of tiles.  Host only; *out is owned by the
  * caller (muon_plan_destroy).  Errors: MUON_EINVAL, MUON_ESHAPE. */
