@@ -478,6 +478,8 @@ def main():
     torch.cuda.synchronize()
 
     timing = not args.no_timing
+    ns_classes = ("gram", "symsq", "prod", "update", "fused")
+    breakdown_steps = min(args.steps, 5)
     if timing:
         # one event pair per launch: size the pool from one step's launches
         # (launches beyond the pool would go untimed); one pool per lane
@@ -490,14 +492,33 @@ def main():
             return tot
         for c in ms.contexts:
             c.timing_enable(True, capacity=1 << 14)
+            c.timing_select(None)
             c.timing_reset()
         ms.step()
-        per = sum(v[1] for v in timing_read().values())
+        pre = timing_read()
+        per = sum(v[1] for v in pre.values())
+        # the dominant Newton-Schulz kernel class by time in that step: the
+        # timed steps record events around its launches only, so the other
+        # launches' event markers stay out of the timed region
+        dom = max(ns_classes, key=lambda k: pre[k][0])
         for c in ms.contexts:
-            c.timing_enable(True, capacity=int(per * args.steps) + 64)
+            c.timing_enable(True, capacity=int(per * max(args.steps, breakdown_steps)) + 64)
+            c.timing_select([dom])
             c.timing_reset()
     ms_per_step, ms_median, ms_min, wall, per = step_times(ms.step, args.steps)
-    kt = timing_read() if timing else {}
+    kd = timing_read() if timing else {}
+    if timing:
+        # the per-class breakdown: a few steps after the timed region with
+        # every launch between events
+        for c in ms.contexts:
+            c.timing_select(None)
+            c.timing_reset()
+        for _ in range(breakdown_steps):
+            ms.step()
+        torch.cuda.synchronize()
+        kt = timing_read()
+    else:
+        kt = {}
 
     units = unit_list(w)
     fl = [ns_flops(m, n, w.ns_steps) for (m, n) in units]
@@ -537,7 +558,7 @@ def main():
     breakdown = {}
     roofline = None
     if timing:
-        per_step = {k: (v[0] / args.steps, v[1] / args.steps) for k, v in kt.items()}
+        per_step = {k: (v[0] / breakdown_steps, v[1] / breakdown_steps) for k, v in kt.items()}
         for k, (t, n) in per_step.items():
             breakdown[k] = {"ms_per_step": round(t, 4), "launches_per_step": n}
         def tf(f, k):
@@ -556,17 +577,19 @@ def main():
             t = per_step[k][0]
             breakdown[k]["gbs"] = round(b / (t * 1e-3) / 1e9, 1) if t > 0 else None
             breakdown[k]["frac_hbm"] = round(b / (t * 1e-3) / 1e9 / PEAK_HBM_GBS, 4) if t > 0 else None
-        # the dominant Newton-Schulz kernel class by time; the HBM counter
-        # records were taken on the default iteration (5 fixed quintic steps,
-        # norms from the momentum pass, automatic fusion) and apply to it only
-        dom = max(("gram", "symsq", "prod", "update", "fused"), key=lambda k: per_step[k][0])
+        # the roofline: the dominant class's launches inside the timed region.
+        # The HBM counter records were taken on the default iteration (5 fixed
+        # quintic steps, norms from the momentum pass, automatic fusion) and
+        # apply to it only
         default_ns = (args.ns_method == "quintic" and args.ns_coeffs == "fixed" and w.ns_steps == 5
                       and args.norms == "momentum" and args.ns_fuse == "auto" and w.compute == "bf16")
-        t_dom, n_dom = per_step[dom]
+        t_dom, n_dom = kd[dom][0] / args.steps, kd[dom][1] / args.steps
         csrc = os.path.join(ROOT, "newton_schulz_amd", "csrc")
         if dom == "fused" and t_dom > 0:
             achieved = fused_hbm / (t_dom * 1e-3) / 1e9
-            breakdown["fused"]["gbs"] = round(achieved, 1)
+            if per_step["fused"][0] > 0:
+                breakdown["fused"]["gbs"] = round(fused_hbm / (per_step["fused"][0] * 1e-3) / 1e9, 1)
+            mfma_tf = ex["fused"] / (t_dom * 1e-3) / 1e12
             traffic = None if not default_ns else traffic_record(f"ns_small_kernel_traffic_{w.name}", n_dom,
                                      os.path.join(csrc, "ns_small.hip"), os.path.join(csrc, "ns_mfma_common.h"),
                                      os.path.join(csrc, "muon_device.h"))
@@ -575,9 +598,8 @@ def main():
                         "kernel": "ns_small_kernel (every iteration of units with m <= 128 in one launch)",
                         "avg_launch_ms": round(t_dom / n_dom, 4),
                         "bytes_per_launch_avg": int(fused_hbm / n_dom),
-                        "mfma_tflops": breakdown["fused"].get("tflops"),
-                        "mfma_frac": round(breakdown["fused"]["tflops"] / PEAK_BF16_TFLOPS, 4)
-                        if breakdown["fused"].get("tflops") else None}
+                        "mfma_tflops": round(mfma_tf, 2),
+                        "mfma_frac": round(mfma_tf / PEAK_BF16_TFLOPS, 4)}
         elif n_dom > 0 and t_dom > 0:
             achieved = ex[dom] / (t_dom * 1e-3) / 1e12
             traffic = None
@@ -633,6 +655,9 @@ def main():
         "matrices_per_s": round(len(units) / (ms_per_step * 1e-3), 1),
         "wall_s_timed": round(wall, 3),
         "breakdown": breakdown,
+        "breakdown_from": (f"{breakdown_steps} steps after the timed region, every launch between HIP events; "
+                           f"the timed steps record events around the {dom} launches only (the roofline's)")
+        if timing else None,
         "roofline": roofline,
     }
     if layers_note is not None:

@@ -407,6 +407,12 @@ typedef enum {
 } muon_kernel_class_t;
 
 muon_status_t muon_timing_enable(muon_ctx_t* ctx, int32_t enable, int32_t capacity);
+/* Time only the kernel classes whose bit (1u << muon_kernel_class_t) is set
+ * in class_mask: launches of the other classes record no events, and so
+ * add no event markers to their stream (every class is timed by default;
+ * 0 times none).  Takes effect for launches enqueued after the call.
+ * Errors: MUON_EINVAL (ctx NULL, or a bit at or above MUON_K_COUNT set). */
+muon_status_t muon_timing_select(muon_ctx_t* ctx, uint32_t class_mask);
 muon_status_t muon_timing_reset(muon_ctx_t* ctx);
 muon_status_t muon_timing_read(muon_ctx_t* ctx, int32_t kernel_class, double* total_ms,
                                int64_t* launches);

@@ -20,7 +20,7 @@ EXPORTS = [
     "muon_ns_workspace_bytes", "muon_plan_create", "muon_plan_num_buckets", "muon_plan_bucket",
     "muon_plan_max_workspace", "muon_plan_destroy", "muon_momentum_update",
     "muon_newton_schulz_batched", "muon_apply", "muon_status_string", "muon_last_error",
-    "muon_timing_enable", "muon_timing_reset", "muon_timing_read",
+    "muon_timing_enable", "muon_timing_select", "muon_timing_reset", "muon_timing_read",
     "muon_newton_schulz_batched_noalloc", "muon_noalloc_last_error",
     "muon_plan", "muon_plan_total_elems", "muon_workspace_bytes",
 ]
@@ -85,6 +85,7 @@ def load() -> ctypes.CDLL:
         "muon_status_string": (ctypes.c_char_p, [i32]),
         "muon_last_error": (ctypes.c_char_p, [vp]),
         "muon_timing_enable": (i32, [vp, i32, i32]),
+        "muon_timing_select": (i32, [vp, ctypes.c_uint32]),
         "muon_timing_reset": (i32, [vp]),
         "muon_timing_read": (i32, [vp, i32, P(ctypes.c_double), P(i64)]),
         "muon_newton_schulz_batched_noalloc": (i32, [ctypes.c_int, vp, P(vp), i64, Shape, i32,

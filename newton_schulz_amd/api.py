@@ -268,6 +268,19 @@ class Context:
     def timing_enable(self, enable: bool = True, capacity: int = 8192):
         self._raise(self.lib.muon_timing_enable(self.handle, 1 if enable else 0, capacity), "timing_enable")
 
+    def timing_select(self, classes=None):
+        """Time only the named kernel classes (names of timing_read); None: all."""
+        names = list(_lib.KERNEL_CLASSES)
+        if classes is None:
+            mask = (1 << len(names)) - 1
+        else:
+            mask = 0
+            for c in classes:
+                if c not in names:
+                    raise ValueError(f"unknown kernel class {c!r}; one of {names}")
+                mask |= 1 << names.index(c)
+        self._raise(self.lib.muon_timing_select(self.handle, mask), "timing_select")
+
     def timing_reset(self):
         self._raise(self.lib.muon_timing_reset(self.handle), "timing_reset")
 

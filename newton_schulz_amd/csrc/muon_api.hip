@@ -50,6 +50,7 @@ struct muon_ctx {
   int tab_next = 0;
   // timing
   bool timing = false;
+  uint32_t tmask = (1u << MUON_K_COUNT) - 1;  // classes that record events
   std::vector<hipEvent_t> tev;
   std::vector<int> tcls;
   size_t tused = 0;  // events recorded (pairs * 2)
@@ -72,7 +73,7 @@ muon_status_t hip_fail(muon_ctx* c, hipError_t e, const char* where) {
 
 // Record the start event of a timed launch; returns the pair index or -1.
 long tstart(muon_ctx* c, hipStream_t s, int cls) {
-  if (!c->timing || c->tused + 2 > c->tev.size()) return -1;
+  if (!c->timing || !((c->tmask >> cls) & 1u) || c->tused + 2 > c->tev.size()) return -1;
   const long k = static_cast<long>(c->tused);
   if (hipEventRecord(c->tev[k], s) != hipSuccess) return -1;
   c->tcls[k / 2] = cls;
@@ -211,6 +212,12 @@ muon_status_t muon_timing_enable(muon_ctx_t* c, int32_t enable, int32_t capacity
   }
   c->tused = 0;
   c->timing = true;
+  return MUON_OK;
+}
+
+muon_status_t muon_timing_select(muon_ctx_t* c, uint32_t class_mask) {
+  if (c == nullptr || (class_mask >> MUON_K_COUNT) != 0) return MUON_EINVAL;
+  c->tmask = class_mask;
   return MUON_OK;
 }
 

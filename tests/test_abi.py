@@ -53,6 +53,12 @@ def test_create_without_gpu_fails_cleanly():
     assert lib.muon_destroy(None) == _lib.MUON_OK
 
 
+def test_timing_select_rejects_null_and_unknown_classes():
+    lib = _lib.load()
+    assert lib.muon_timing_select(None, 1) == _lib.MUON_EINVAL
+    assert lib.muon_timing_select(None, 1 << len(_lib.KERNEL_CLASSES)) == _lib.MUON_EINVAL
+
+
 def test_struct_and_enum_mirrors_match_header():
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
     body = re.search(r"typedef struct \{([^}]*)\} muon_ns_params_t;", text).group(1)
