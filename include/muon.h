@@ -193,8 +193,10 @@ muon_status_t muon_ns_minimax_coeffs(int32_t steps, double lo, double margin, fl
  * residual (2 bytes per element, rows and columns padded to the tile: 256
  * once m >= 256, else 128) and B's diagonal in fp32 (4 m).  Each region is
  * rounded up to 256 bytes: (2 + 2 m/n) x the unit's e m n bytes (BF16:
- * 3 + 2 m/n, up to the residual's padding) plus scalars.  Returns 0 for an
- * invalid shape or count <= 0. */
+ * 3 + 2 m/n, up to the residual's padding) plus scalars.  BF16 units with
+ * m < 16 run the iteration in fp32: for them it is at least the inputs
+ * widened to fp32 (4 m n) plus the F32 figure.  Returns 0 for an invalid
+ * shape or count <= 0. */
 size_t muon_ns_workspace_bytes(muon_shape_t shape, int64_t count, int32_t compute);
 
 /* Workspace to run Newton-Schulz over a list of matrices of mixed shapes,
@@ -327,7 +329,9 @@ muon_status_t muon_momentum_update_sq(muon_ctx_t* ctx, void* stream, const void*
  * out[i] == mats[i], means in place).  With shape.head_rows = h > 0 every
  * h x cols row block is orthogonalised on its own.  Supported (io_dtype,
  * params->compute): (BF16, BF16) -- bf16 MFMA, fp32 accumulate, A, B and
- * the X iterates rounded to bf16; (F32, F32) -- fp32 verification mode.
+ * the X iterates rounded to bf16 (units whose smaller side is under 16:
+ * the iteration in fp32 on widened inputs, the result rounded to bf16);
+ * (F32, F32) -- fp32 verification mode.
  * The Frobenius norm is reduced deterministically (fixed order), so two
  * calls on identical inputs give identical bits.  A unit whose norm is 0
  * yields exactly 0.  nonfinite_flag (device int, may be NULL) gets 1 OR-ed

@@ -489,6 +489,35 @@ muon_status_t ns_batched(const NsEnv& env, void* stream, const void* const* mats
     c->tab_used[slot] = true;
   }
 
+  // BF16 units whose smaller side is under kNsTinySide run the iteration in
+  // fp32: their bf16 A and B' alone take some Gaussian draws past the bf16
+  // error bar.  The inputs are widened into the slab, the fp32 call runs in
+  // place there (norms recomputed from the same values), and its result is
+  // rounded to bf16 into the outputs.
+  if (prm->compute == MUON_BF16 && L.m < kNsTinySide) {
+    char* stage = env.ws + L.stage;
+    const MatRef SR{stage, unit_elems * 4, nullptr};
+    e = launch_convert(s, in.ref, 1, SR, 0, unit_elems, L.units, nullptr);
+    if (e != hipSuccess) return ehip(env, e, "widen launch");
+    std::vector<const void*> sp(static_cast<size_t>(L.units));
+    for (int64_t i = 0; i < L.units; ++i) sp[static_cast<size_t>(i)] = stage + i * unit_elems * 4;
+    muon_ns_params_t p32 = *prm;
+    p32.compute = MUON_F32;
+    p32.sq_partials = nullptr;
+    p32.sq_base = nullptr;
+    p32.sq_count = 0;
+    NsEnv sub = env;
+    sub.ws = env.ws + L.sub;
+    sub.ws_bytes = env.ws_bytes - L.sub;
+    sub.outputs_in_place = true;
+    const muon_shape_t us{L.ur, L.uc, 0};
+    const muon_status_t st =
+        ns_batched(sub, stream, sp.data(), L.units, us, MUON_F32, &p32, nullptr, nonfinite_flag);
+    if (st != MUON_OK) return st;
+    e = launch_convert(s, SR, 0, ot.ref, 1, unit_elems, L.units, nullptr);
+    return e == hipSuccess ? MUON_OK : ehip(env, e, "narrow launch");
+  }
+
   char* ws = env.ws;
   const int64_t xbytes = L.m * L.n * static_cast<int64_t>(es);
   const int64_t abytes = L.m * L.m * static_cast<int64_t>(es);

@@ -102,6 +102,10 @@ hipError_t launch_compact_units(hipStream_t s, const int* zflag, int64_t units, 
 // out[u] = s[u] * in[u], element-wise over units of unit_elems (steps == 0, copies).
 hipError_t launch_scale_copy(hipStream_t s, MatRef in, MatRef out, int64_t unit_elems,
                              int64_t units, const float* scale, int io_bf16);
+// The same, read as bf16 or fp32 (in_bf16) and stored as bf16 (rounded to
+// nearest even) or fp32 (out_bf16); scale may be null (factor 1).
+hipError_t launch_convert(hipStream_t s, MatRef in, int in_bf16, MatRef out, int out_bf16,
+                          int64_t unit_elems, int64_t units, const float* scale);
 
 // bf16 MFMA path (all of M, N, K, leading dims multiples of 8; 16-byte aligned
 // bases; each operand smaller than 2 GiB).  tile: 128 or 256.

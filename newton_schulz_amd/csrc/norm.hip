@@ -179,16 +179,18 @@ __global__ __launch_bounds__(256) void compact_units_kernel(const int* __restric
   if (threadIdx.x == 0) *count = static_cast<int>(base);
 }
 
-template <typename T>
+// out[u] = s[u] * in[u] element by element (s = 1 without scale), read as Ti
+// and stored as To (bf16: rounded to nearest even)
+template <typename Ti, typename To>
 __global__ __launch_bounds__(256) void scale_copy_kernel(MatRef in, MatRef out, int64_t n,
                                                          const float* scale) {
   const int64_t u = blockIdx.y;
-  const T* src = reinterpret_cast<const T*>(mat_at(in, u));
-  T* dst = reinterpret_cast<T*>(mat_at(out, u));
+  const Ti* src = reinterpret_cast<const Ti*>(mat_at(in, u));
+  To* dst = reinterpret_cast<To*>(mat_at(out, u));
   const float s = scale ? scale[u] : 1.0f;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
        e += static_cast<int64_t>(gridDim.x) * 256) {
-    muon::Elem<T>::store(dst + e, s * muon::Elem<T>::load(src + e));
+    muon::Elem<To>::store(dst + e, s * muon::Elem<Ti>::load(src + e));
   }
 }
 
@@ -241,6 +243,11 @@ hipError_t launch_compact_units(hipStream_t s, const int* zflag, int64_t units, 
 
 hipError_t launch_scale_copy(hipStream_t s, MatRef in, MatRef out, int64_t unit_elems,
                              int64_t units, const float* scale, int io_bf16) {
+  return launch_convert(s, in, io_bf16, out, io_bf16, unit_elems, units, scale);
+}
+
+hipError_t launch_convert(hipStream_t s, MatRef in, int in_bf16, MatRef out, int out_bf16,
+                          int64_t unit_elems, int64_t units, const float* scale) {
   if (units == 0 || unit_elems == 0) return hipSuccess;
   int64_t bx = (unit_elems + 255) / 256;
   if (bx > 1024) bx = 1024;
@@ -250,8 +257,10 @@ hipError_t launch_scale_copy(hipStream_t s, MatRef in, MatRef out, int64_t unit_
     dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(n));
     const MatRef i0 = shifted(in, u0), o0 = shifted(out, u0);
     const float* s0 = scale ? scale + u0 : nullptr;
-    if (io_bf16) scale_copy_kernel<bf16_t><<<grid, 256, 0, s>>>(i0, o0, unit_elems, s0);
-    else scale_copy_kernel<float><<<grid, 256, 0, s>>>(i0, o0, unit_elems, s0);
+    if (in_bf16 && out_bf16) scale_copy_kernel<bf16_t, bf16_t><<<grid, 256, 0, s>>>(i0, o0, unit_elems, s0);
+    else if (in_bf16) scale_copy_kernel<bf16_t, float><<<grid, 256, 0, s>>>(i0, o0, unit_elems, s0);
+    else if (out_bf16) scale_copy_kernel<float, bf16_t><<<grid, 256, 0, s>>>(i0, o0, unit_elems, s0);
+    else scale_copy_kernel<float, float><<<grid, 256, 0, s>>>(i0, o0, unit_elems, s0);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

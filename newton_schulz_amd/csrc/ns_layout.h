@@ -17,12 +17,18 @@
 //            m >= 256, else 128 x 128, which also holds the 128-tiles that
 //            ns_mfma_tile may pick for m >= 256)
 //   dvec     float per unit and row of A    diagonal of B' before rounding
+// BF16 units whose smaller side is under kNsTinySide run the iteration in
+// fp32 instead (their bf16 A and B' alone take some Gaussian draws past the
+// bf16 error bar): the slab then starts with the inputs widened to fp32
+// (stage, 4 bytes per element), followed at `sub` by the fp32 layout of the
+// same units; total covers both layouts.
+constexpr int64_t kNsTinySide = 16;
 struct NsLayout {
   int64_t units = 0, ur = 0, uc = 0, m = 0, n = 0;
   int parts = 1;  // norm partial sums per unit
   size_t lo_unit = 0;  // residual plane bytes per unit
   size_t xa = 0, xb = 0, a = 0, b = 0, scale = 0, zflag = 0, partial = 0, lo = 0, dvec = 0,
-         total = 0;
+         stage = 0, sub = 0, total = 0;
 };
 
 bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* L);

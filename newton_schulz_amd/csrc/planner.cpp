@@ -107,6 +107,16 @@ bool ns_layout(const muon_shape_t& s, int64_t count, int32_t compute, NsLayout* 
     l.lo = off; off += align_up(U * l.lo_unit);
     l.dvec = off; off += align_up(U * static_cast<size_t>(l.m) * 4);
   }
+  if (compute == MUON_BF16 && l.m < kNsTinySide) {
+    // the fp32 iteration of small units: their widened inputs, then the
+    // fp32 layout of the same call
+    NsLayout f;
+    const muon_shape_t one{l.ur, l.uc, 0};
+    if (!ns_layout(one, l.units, MUON_F32, &f)) return false;
+    l.stage = 0;
+    l.sub = align_up(U * static_cast<size_t>(ue) * 4);
+    off = std::max(off, l.sub + f.total);
+  }
   l.total = count == 0 ? 0 : off;
   *L = l;
   return true;

@@ -150,6 +150,16 @@ def test_ns_bf16_generic_shapes(ctx, rows, cols):
     ns_check(ctx, rows, cols, 2, torch.bfloat16, BF16_TOL, seed=rows * 3 + cols)
 
 
+# degenerate shapes: one row or column (the normalised unit is its own polar
+# factor's direction with singular value 1), a single element, shapes far
+# below one tile, and sides that are not multiples of 8 (generic kernels)
+@pytest.mark.parametrize("rows,cols", [(1, 1), (1, 64), (64, 1), (1, 7), (3, 5), (5, 3), (8, 8), (1, 4096),
+                                       (4096, 1), (2, 2)])
+def test_ns_degenerate_shapes(ctx, rows, cols):
+    ns_check(ctx, rows, cols, 2, torch.bfloat16, BF16_TOL, seed=rows * 7 + cols)
+    ns_check(ctx, rows, cols, 2, torch.float32, F32_TOL, seed=rows * 7 + cols, std=1.0)
+
+
 @pytest.mark.parametrize("steps", [0, 1, 2, 6])
 def test_ns_step_counts(ctx, steps):
     ns_check(ctx, 256, 512, 2, torch.bfloat16, BF16_TOL, seed=steps, steps=steps)
