@@ -160,6 +160,12 @@ def test_ns_degenerate_shapes(ctx, rows, cols):
     ns_check(ctx, rows, cols, 2, torch.float32, F32_TOL, seed=rows * 7 + cols, std=1.0)
 
 
+# heads of fewer than 16 rows take the fp32 iteration too, per head
+@pytest.mark.parametrize("rows,cols,h", [(64, 96, 8), (24, 40, 4), (48, 3, 16)])
+def test_ns_small_heads(ctx, rows, cols, h):
+    ns_check(ctx, rows, cols, 2, torch.bfloat16, BF16_TOL, head_rows=h, seed=rows + cols + h)
+
+
 @pytest.mark.parametrize("steps", [0, 1, 2, 6])
 def test_ns_step_counts(ctx, steps):
     ns_check(ctx, 256, 512, 2, torch.bfloat16, BF16_TOL, seed=steps, steps=steps)
