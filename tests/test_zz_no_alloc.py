@@ -47,6 +47,7 @@ CALLS = [
     [(512, 1024, 3, 128, {}), (256, 640, 2, 128, {})],                    # per-head
     [(520, 1048, 2, 0, {"method": "gram"}), (264, 520, 2, 0, {"coeffs": "minimax"})],
     [(96, 160, 3, 0, {"compute": "f32"}), (40, 72, 2, 0, {"compute": "f32"})],
+    [(8, 64, 5, 0, {}), (24, 40, 2, 4, {})],                              # units under 16: fp32 iteration
 ]
 
 
