@@ -399,6 +399,8 @@ def main():
     ap.add_argument("--pageable", action="store_true", help="--offload: pageable host memory")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip per-kernel event timing")
+    ap.add_argument("--graph", action="store_true",
+                    help="record the step into a HIP graph once and time its replays (no per-kernel timing)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (HBM counter calibration)")
     args = ap.parse_args()
@@ -436,6 +438,9 @@ def main():
         args.inflight = 2 if args.offload else 1
     if args.inflight < 1:
         print("--inflight must be >= 1", file=sys.stderr)
+        sys.exit(2)
+    if args.graph and (args.offload or args.library_gemm):
+        print("--graph records the resident step only", file=sys.stderr)
         sys.exit(2)
     layers_note = None
     if args.workload in ("qwen3_30b_experts:fit", "qwen3_30b_experts:48"):
@@ -476,8 +481,16 @@ def main():
     for _ in range(args.warmup):
         ms.step()
     torch.cuda.synchronize()
+    run = ms.step
+    if args.graph:
+        # the whole step as one recorded graph; replays record no per-kernel
+        # events, so this line carries no breakdown or roofline
+        ms.capture()
+        ms.replay()
+        torch.cuda.synchronize()
+        run = ms.replay
 
-    timing = not args.no_timing
+    timing = not args.no_timing and not args.graph
     ns_classes = ("gram", "symsq", "prod", "update", "fused")
     breakdown_steps = min(args.steps, 5)
     if timing:
@@ -505,7 +518,7 @@ def main():
             c.timing_enable(True, capacity=int(per * max(args.steps, breakdown_steps)) + 64)
             c.timing_select([dom])
             c.timing_reset()
-    ms_per_step, ms_median, ms_min, wall, per = step_times(ms.step, args.steps)
+    ms_per_step, ms_median, ms_min, wall, per = step_times(run, args.steps)
     kd = timing_read() if timing else {}
     if timing:
         # the per-class breakdown: a few steps after the timed region with
@@ -646,7 +659,7 @@ def main():
                    "ns_fuse": args.ns_fuse,
                    "micro_bucket_cap_bytes": w.cap_bytes, "cap_kind": w.cap_kind,
                    "micro_buckets": len(ms.plan.buckets), "workspace_bytes": ms.plan.max_workspace,
-                   "inflight_micro_buckets": args.inflight,
+                   "inflight_micro_buckets": args.inflight, "graph_replay": bool(args.graph),
                    "parallelism": "single GPU"},
         "frac_of_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "ns_tflop_per_step_algorithmic": round(f_ns / 1e12, 4),

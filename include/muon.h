@@ -337,8 +337,12 @@ muon_status_t muon_momentum_update_sq(muon_ctx_t* ctx, void* stream, const void*
  * yields exactly 0.  nonfinite_flag (device int, may be NULL) gets 1 OR-ed
  * in when some unit's norm is not finite; values are propagated, never
  * skipped.  Uses the context workspace (muon_ns_workspace_bytes(shape,
- * count, compute) bytes).  count == 0 is a no-op.  Errors: MUON_EINVAL,
- * MUON_ESHAPE, MUON_EDTYPE, MUON_EWORKSPACE, MUON_EHIP. */
+ * count, compute) bytes).  count == 0 is a no-op.  The call may be recorded
+ * into a HIP graph (stream capture) when the inputs, and the outputs, are
+ * evenly spaced; irregularly placed matrices need pointer tables uploaded
+ * from a host ring that later calls reuse, and are rejected while the
+ * stream captures (MUON_EINVAL).  Errors: MUON_EINVAL, MUON_ESHAPE,
+ * MUON_EDTYPE, MUON_EWORKSPACE, MUON_EHIP. */
 muon_status_t muon_newton_schulz_batched(muon_ctx_t* ctx, void* stream, const void* const* mats,
                                          int64_t count, muon_shape_t shape, int32_t io_dtype,
                                          const muon_ns_params_t* params, void* const* out,
@@ -395,8 +399,8 @@ const char* muon_last_error(const muon_ctx_t* ctx);
 
 /* Per-kernel-class timing with HIP events recorded on the launch stream
  * around each kernel (per-bucket timing, blog section "Metrics to record").
- * enable != 0 preallocates an event pool; launches beyond its capacity are
- * not timed.  muon_timing_read synchronises on the recorded events and
+ * enable != 0 preallocates an event pool; launches beyond its capacity, and
+ * launches recorded into a graph (stream capture), are not timed.  muon_timing_read synchronises on the recorded events and
  * returns the summed duration and number of timed launches of one class. */
 typedef enum {
   MUON_K_MOMENTUM = 0,

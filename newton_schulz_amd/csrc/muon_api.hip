@@ -74,6 +74,10 @@ muon_status_t hip_fail(muon_ctx* c, hipError_t e, const char* where) {
 // Record the start event of a timed launch; returns the pair index or -1.
 long tstart(muon_ctx* c, hipStream_t s, int cls) {
   if (!c->timing || !((c->tmask >> cls) & 1u) || c->tused + 2 > c->tev.size()) return -1;
+  // launches recorded into a graph are not timed (the events would be
+  // re-recorded by every replay)
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return -1;
   const long k = static_cast<long>(c->tused);
   if (hipEventRecord(c->tev[k], s) != hipSuccess) return -1;
   c->tcls[k / 2] = cls;
@@ -462,6 +466,12 @@ muon_status_t ns_batched(const NsEnv& env, void* stream, const void* const* mats
   hipError_t e;
 
   if (in.needs_table || ot.needs_table) {
+    // the tables are uploaded from a host ring that later calls reuse: a
+    // replayed graph would copy whatever the ring holds then
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(static_cast<hipStream_t>(stream), &cs) != hipSuccess ||
+        cs != hipStreamCaptureStatusNone)
+      return efail(env, MUON_EINVAL, "matrices not evenly spaced: their pointer tables cannot be recorded into a graph");
     const int slot = c->tab_next;
     c->tab_next = (c->tab_next + 1) % kTabSlots;
     if (c->tab_used[slot]) {

@@ -167,6 +167,30 @@ class MuonStep:
                               sq=(sq, upd) if whole else None)
         ctx.apply(master, upd, self.lr, self.scale, self.weight_decay, wb, stream)
 
+    def capture(self, nonfinite_flag: Optional[torch.Tensor] = None) -> "torch.cuda.CUDAGraph":
+        """Record one whole step, every lane's launches included, into a HIP
+        graph (stream capture through torch.cuda.CUDAGraph); replay() then
+        runs it with no host work per launch.  Recording runs nothing.  The
+        graph keeps what the step passed when it was recorded: lr, beta,
+        scale and weight decay, and the state buffers' addresses (their
+        contents are read at replay).  Per-kernel timing skips recorded
+        launches.  Record again after changing a hyperparameter."""
+        g = torch.cuda.CUDAGraph()
+        cur = torch.cuda.current_stream(self.device)
+        side = torch.cuda.Stream(self.device)
+        side.wait_stream(cur)
+        with torch.cuda.graph(g, stream=side):
+            self.step(stream=side, nonfinite_flag=nonfinite_flag)
+        cur.wait_stream(side)
+        self._graph = g
+        return g
+
+    def replay(self):
+        """Run the step recorded by capture() on the current stream."""
+        if getattr(self, "_graph", None) is None:
+            raise RuntimeError("no recorded step: call capture() first")
+        self._graph.replay()
+
     @property
     def contexts(self) -> List[Context]:
         """The lanes' contexts (per-kernel timing is kept per context)."""
