@@ -79,6 +79,8 @@ def test_timing_skips_recorded_launches():
     c.close()
 
 
+# the rejected call records nothing, so torch reports an empty graph
+@pytest.mark.filterwarnings("ignore:The CUDA Graph is empty")
 def test_irregular_placement_cannot_be_recorded():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
