@@ -546,15 +546,16 @@ def main():
     value = f_ns / (ms_per_step * 1e-3) / 1e12
     ex = {"gram": 0, "symsq": 0, "prod": 0, "update": 0, "fused": 0}
     fused_hbm = 0
-    # units the library ran as one fused launch (small wide bf16 units; every
-    # such call in these workloads has a unit per CU)
+    # units the library ran as fused launches (wide bf16 units with 16 <= m <=
+    # 128: in these workloads every such call fuses, by its unit count or its
+    # width)
     fused_ran = timing and kt["fused"][1] > 0
     for (m, n, wide) in unit_list(w, wide_flag=True):
         if args.ns_method == "gram" and uses_gram_form(m, n, w.compute):
             fg, fs, fp, fu = ns_flops_gram(m, n, w.ns_steps)
         else:
             (fg, fs, fu), fp = ns_flops(m, n, w.ns_steps), 0
-        if fused_ran and w.compute == "bf16" and wide and m <= 128:
+        if fused_ran and w.compute == "bf16" and wide and 16 <= m <= 128:
             ex["fused"] += fg + fs + fp + fu
             fused_hbm += fused_bytes(m, n, w.ns_steps, args.ns_method == "gram")
             continue

@@ -74,8 +74,11 @@ typedef enum { MUON_NS_QUINTIC = 0, MUON_NS_GRAM = 1 } muon_ns_method_t;
  * reads the input twice and writes the result once in all.  Results are
  * bit-identical to the unfused kernels.  AUTO fuses when the call has at
  * least as many units as the device has compute units (every CU gets a
- * unit); ON whenever eligible; OFF never.  Not eligible: tall units,
- * m > 128, F32 compute, a per-iteration coefficient table of more than
+ * unit), or when n <= 3072 (a workgroup then finishes its unit before the
+ * separate launches would, however many CUs stay idle); ON whenever
+ * eligible; OFF never.  Not eligible: tall units, m < 16 (those run in
+ * fp32, see muon_newton_schulz_batched), m > 128, F32 compute, a
+ * per-iteration coefficient table of more than
  * MUON_NS_FUSED_MAX_ROWS rows, and outputs that overlap an input other than
  * their own (in place, unit for unit, is fine). */
 typedef enum { MUON_FUSE_AUTO = 0, MUON_FUSE_OFF = 1, MUON_FUSE_ON = 2 } muon_fuse_t;

@@ -626,7 +626,13 @@ muon_status_t ns_batched(const NsEnv& env, void* stream, const void* const* mats
                         (prm->coeffs == nullptr || prm->steps <= MUON_NS_FUSED_MAX_ROWS) &&
                         (!alias || (c == nullptr ? env.outputs_in_place
                                                  : !cross_overlap(mats, outp, count, unit_bytes * per)));
-  if (small_ok && (prm->fuse == MUON_FUSE_ON || L.units >= env.cus)) {
+  // AUTO: a unit for every CU, or units narrow enough that one workgroup per
+  // unit finishes before the separate launches would with most CUs idle
+  // (MI355X, 8 waves per workgroup: ~0.05 + 0.0155 ms per 128-column block
+  // and round of units, against >= 0.28 ms for the fifteen launches; at
+  // 128 x 4096 with a few units the separate launches win)
+  constexpr int64_t kFuseAnyCols = 3072;
+  if (small_ok && (prm->fuse == MUON_FUSE_ON || L.units >= env.cus || n <= kFuseAnyCols)) {
     NsSmallArgs fa{};
     fa.src = in.ref;
     fa.dst = ot.ref;

@@ -235,12 +235,17 @@ def test_fused_eligibility(ctx):
     assert nf == 0
     for x, y in zip(ref, outs):
         assert torch.equal(x, y)
-    # auto: fused once the call has a unit for every compute unit
+    # auto: fused for units of at most 3072 columns, and for wider ones once
+    # the call has a unit for every compute unit
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     few = [synth.normal((128, 256), 1e-3, g, DEV, torch.bfloat16) for _ in range(2)]
     nf, _ = launches(ctx, lambda: ctx.newton_schulz(few, [torch.empty_like(t) for t in few], 0, ns_params()))
+    assert nf == 1
+    wide_few = [synth.normal((128, 4096), 1e-3, g, DEV, torch.bfloat16) for _ in range(2)]
+    nf, _ = launches(ctx, lambda: ctx.newton_schulz(wide_few, [torch.empty_like(t) for t in wide_few], 0,
+                                                    ns_params()))
     assert nf == 0
-    many = synth.normal((cus, 128, 256), 1e-3, g, DEV, torch.bfloat16)
+    many = synth.normal((cus, 128, 3200), 1e-3, g, DEV, torch.bfloat16)
     mm = list(many.unbind(0))
     nf, _ = launches(ctx, lambda: ctx.newton_schulz(mm, [torch.empty_like(t) for t in mm], 0, ns_params()))
     assert nf == 1
@@ -313,11 +318,10 @@ def test_step_merges_head_units_bit_identical():
     wb = torch.empty(ms.numel, dtype=torch.bfloat16, device=DEV)
     c.apply(master, upd, w.lr, 1.0, 0.0, wb)
     torch.cuda.synchronize()
-    # 288 units in one call take the fused launch; 192 q and 96 k/v heads
-    # per call stay below one unit per CU and run as separate launches
-    cus = torch.cuda.get_device_properties(DEV).multi_processor_count
-    assert ms.ctx.timing_read()["fused"][1] == (1 if 288 >= cus else 0)
-    assert c.timing_read()["fused"][1] == (len(by_shape) if 96 >= cus else 0)
+    # 128 x 2560 units fuse at any count: one fused launch for the 288 units
+    # of the merged call, one per shape for the per-matrix calls
+    assert ms.ctx.timing_read()["fused"][1] == 1
+    assert c.timing_read()["fused"][1] == len(by_shape)
     assert torch.equal(ms.momentum, mom)
     assert torch.equal(ms.master, master)
     assert torch.equal(ms.weight_bf16, wb)
